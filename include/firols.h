@@ -1,0 +1,157 @@
+/*
+ * firols.h -- overlap-save FIR filtering on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of the page "一种基于GPU的高阶数字FIR滤波器频域并行
+ * 处理实现方法" (a GPU frequency-domain parallel method for high-order FIR
+ * filters), claim 1:
+ *   step 1  H = N-point DFT of the M taps zero-padded to N, or H given
+ *           directly, kept in GPU memory;
+ *   step 2  the input of a call is cut into blocks B_i of L samples;
+ *   step 3  E_0 = {S0, B_0}, E_i = {D_(i-1), B_i}, where D_i is the last
+ *           M-1 samples of B_i; D_(k-1) becomes the state S0 of the next call;
+ *   step 4  F_i = FFT_N(E_i), I_i = F_i * H, R_i = IFFT_N(I_i);
+ *   step 5  R_i = {Z_i, Y_i}: the first M-1 points Z_i are dropped and the
+ *           L points Y_i are the output;
+ *   step 6  the next input is processed the same way.
+ * With N = L + M - 1 every kept point equals the linear convolution of the
+ * taps with the stream {S0, X}:
+ *       y[t] = sum_{m<M} h[m] * xt[t-m],  xt[j] = S0[M-1+j] for j < 0.
+ *
+ * Data types.  Samples are complex64: interleaved (re, im) float32 pairs.
+ * The state S0 of a channel is M-1 samples in time order (S0[0] oldest).
+ * Channel c of a [nchan][chan_stride] array starts at element c*chan_stride.
+ *
+ * Status.  Every function returns FIR_OLS_OK (0) or a negative status.  A
+ * call that returns an error has enqueued nothing and changed nothing,
+ * except FIR_OLS_ERR_HIP after a launch, which reports what the HIP runtime
+ * said.  No function aborts or prints.
+ *
+ * Devices and streams.  A plan lives on the HIP device that was current
+ * when it was created; every later call must be made with that device
+ * current.  Stream arguments are hipStream_t values passed as void*; NULL
+ * means the device's null stream.  A plan holds one filter state, so calls
+ * on one plan must be ordered (one stream, or streams the caller orders).
+ * Different plans are independent.
+ */
+#ifndef FIROLS_H
+#define FIROLS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fir_ols_plan_s *fir_ols_plan_t;   /* opaque, library-owned */
+
+enum {
+    FIR_OLS_OK = 0,
+    FIR_OLS_ERR_INVALID_ARG = -1,  /* null handle/pointer, bad size or stride */
+    FIR_OLS_ERR_UNSUPPORTED = -2,  /* size outside what the kernels cover */
+    FIR_OLS_ERR_NO_FILTER = -3,    /* execute before set_taps/set_freq_response */
+    FIR_OLS_ERR_ALIAS = -4,        /* input and output memory overlap */
+    FIR_OLS_ERR_ALIGN = -5,        /* device pointer not 8-byte aligned */
+    FIR_OLS_ERR_OOM = -6,          /* device allocation failed */
+    FIR_OLS_ERR_HIP = -7,          /* HIP runtime error (launch, copy, sync) */
+    FIR_OLS_ERR_DEVICE = -8        /* current device is not the plan's device */
+};
+
+/*
+ * Create a plan for M taps and N-point blocks (claim 1, steps 1-2: N is the
+ * transform length, the block length is L = N - M + 1).
+ *   out    receives the handle (set to NULL on error).
+ *   M      taps, 1 <= M <= N.
+ *   N      power of two, 8 <= N <= 65536.
+ *   nchan  independent channels sharing the filter, nchan >= 1; each has
+ *          its own state.
+ * Allocates the frequency response (aligned to 256 bytes, the page's
+ * alignment rule in step 1), the twiddle tables and two state buffers of
+ * nchan*(M-1) samples on the current device.  The state starts at zero.
+ * No filter is set yet.  Synchronous.
+ */
+int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan);
+
+/*
+ * Set the filter from its taps (claim 1, step 1, first case): the taps are
+ * zero-padded to N and transformed on the GPU; H is kept scaled by 1/N so
+ * the inverse transform of step 4 needs no separate scaling.
+ *   h_host      host array: M float32 taps (is_complex == 0) or M
+ *               interleaved complex64 taps (is_complex != 0); copied
+ *               before return, the caller keeps ownership.
+ *   M           must equal the plan's M.
+ *   stream      stream the work is ordered on (after earlier executes).
+ * Returns after H is in place.  Leaves the state unchanged.
+ */
+int fir_ols_set_taps(fir_ols_plan_t p, const float *h_host, int64_t M,
+                     int is_complex, void *stream);
+
+/*
+ * Set the filter from its frequency response (claim 1, step 1, second
+ * case).
+ *   H_host  host array of N interleaved complex64 values: the unscaled
+ *           forward DFT (kernel exp(-2 pi j q m / N)) of the zero-padded
+ *           taps, bin 0 first.  Copied before return.
+ *   N       must equal the plan's N.
+ * The library applies the 1/N factor itself.  H is not checked for being
+ * the response of an M-tap filter; if it is not, each output is the
+ * circular convolution of its block E_i with IDFT(H) at index M-1+t.
+ * Returns after H is in place.  Leaves the state unchanged.
+ */
+int fir_ols_set_freq_response(fir_ols_plan_t p, const float *H_host,
+                              int64_t N, void *stream);
+
+/*
+ * Filter one call's input (claim 1, steps 2-5, with the state carry of
+ * step 3).
+ *   x_dev        device complex64 input, [nchan][chan_stride]; the first
+ *                nsamples of every channel are read.
+ *   y_dev        device complex64 output, same layout; the first nsamples
+ *                of every channel are written, nothing else is touched.
+ *   nsamples     samples per channel in this call, >= 0.  Any count is
+ *                accepted: the last block may be partial (it is padded
+ *                with zeros, which only reach dropped outputs).  0 is a
+ *                no-op that leaves the state as it is.
+ *   chan_stride  elements between channel starts, >= nsamples.
+ *   stream       the call is enqueued on it and returns without waiting.
+ * Both pointers must be 8-byte aligned and the two ranges must not
+ * overlap (in-place filtering would let one block overwrite the overlap
+ * another block still reads).  The state of every channel becomes the last
+ * M-1 samples of {S0, x} of that channel.
+ */
+int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev,
+                    int64_t nsamples, int64_t chan_stride, void *stream);
+
+/*
+ * Replace the state (claim 1, step 3: S0 is the M-1 samples that preceded
+ * the call).
+ *   s0_dev  device complex64 [nchan][M-1], time order, or NULL for zeros.
+ * Stream-ordered and asynchronous.  With M == 1 there is no state and the
+ * call is a no-op.
+ */
+int fir_ols_set_state(fir_ols_plan_t p, const void *s0_dev, void *stream);
+
+/*
+ * Copy the current state out, e.g. to checkpoint a stream and resume it in
+ * another plan with fir_ols_set_state.
+ *   s0_out_dev  device complex64 [nchan][M-1].
+ * Stream-ordered and asynchronous.
+ */
+int fir_ols_get_state(fir_ols_plan_t p, void *s0_out_dev, void *stream);
+
+/*
+ * Destroy a plan: waits for the plan's device to finish, then frees its
+ * buffers.  NULL is a no-op.
+ */
+int fir_ols_destroy(fir_ols_plan_t p);
+
+/* Block length L = N - M + 1 of a plan, or a negative status. */
+int64_t fir_ols_block_length(fir_ols_plan_t p);
+
+/* Static text for a status code. */
+const char *fir_ols_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FIROLS_H */

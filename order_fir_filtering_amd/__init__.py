@@ -1,0 +1,236 @@
+"""Overlap-save FIR filtering on AMD Instinct MI355X (gfx950).
+
+Thin Python binding of ``libfirols.so``: the functions below carry the C
+names of ``include/firols.h`` and only marshal arguments (pointers, sizes,
+streams).  Every step of the filtering runs in the library's HIP kernels.
+If the library is not built, loading raises ``FirOlsError``: there is no
+fallback of any kind.
+
+Pointers may be given as integers or as torch tensors (their ``data_ptr``);
+streams as integers, torch streams, or ``None`` (torch's current stream on
+the current device when torch has CUDA/HIP, else the null stream).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+from .build import LIB as LIBRARY_PATH
+
+__all__ = [
+    "FirOlsError", "Plan", "load_library", "LIBRARY_PATH", "EXPORTED",
+    "fir_ols_plan", "fir_ols_set_taps", "fir_ols_set_freq_response",
+    "fir_ols_execute", "fir_ols_set_state", "fir_ols_get_state",
+    "fir_ols_destroy", "fir_ols_block_length", "fir_ols_status_string",
+]
+
+# Every symbol include/firols.h declares.
+EXPORTED = (
+    "fir_ols_plan", "fir_ols_set_taps", "fir_ols_set_freq_response",
+    "fir_ols_execute", "fir_ols_set_state", "fir_ols_get_state",
+    "fir_ols_destroy", "fir_ols_block_length", "fir_ols_status_string",
+)
+
+STATUS = {
+    0: "FIR_OLS_OK", -1: "FIR_OLS_ERR_INVALID_ARG", -2: "FIR_OLS_ERR_UNSUPPORTED",
+    -3: "FIR_OLS_ERR_NO_FILTER", -4: "FIR_OLS_ERR_ALIAS", -5: "FIR_OLS_ERR_ALIGN",
+    -6: "FIR_OLS_ERR_OOM", -7: "FIR_OLS_ERR_HIP", -8: "FIR_OLS_ERR_DEVICE",
+}
+
+
+class FirOlsError(RuntimeError):
+    def __init__(self, status: int, where: str = ""):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        msg = self.name if status in STATUS else f"status {status}"
+        if _lib is not None and status in STATUS:
+            msg += ": " + _lib.fir_ols_status_string(status).decode()
+        super().__init__(f"{where}: {msg}" if where else msg)
+
+
+_lib = None
+_vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+
+
+def load_library(path: Optional[str] = None):
+    """Load libfirols.so (built in-tree by order_fir_filtering_amd.build)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or LIBRARY_PATH
+    if not os.path.exists(path):
+        raise FirOlsError(-7, f"{path} is not built (run order_fir_filtering_amd.build.build())")
+    lib = ctypes.CDLL(path)
+    sig = {
+        "fir_ols_plan": (_int, [ctypes.POINTER(_vp), _i64, _i64, _i64]),
+        "fir_ols_set_taps": (_int, [_vp, _vp, _i64, _int, _vp]),
+        "fir_ols_set_freq_response": (_int, [_vp, _vp, _i64, _vp]),
+        "fir_ols_execute": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
+        "fir_ols_set_state": (_int, [_vp, _vp, _vp]),
+        "fir_ols_get_state": (_int, [_vp, _vp, _vp]),
+        "fir_ols_destroy": (_int, [_vp]),
+        "fir_ols_block_length": (_i64, [_vp]),
+        "fir_ols_status_string": (ctypes.c_char_p, [_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    if path == LIBRARY_PATH:
+        _lib = lib
+    return lib
+
+
+def _ptr(p) -> Optional[int]:
+    if p is None:
+        return None
+    if hasattr(p, "data_ptr"):
+        return int(p.data_ptr())
+    return int(p)
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        try:
+            import torch
+            if torch.cuda.is_available():
+                return int(torch.cuda.current_stream().cuda_stream) or None
+        except ImportError:
+            pass
+        return None
+    if hasattr(s, "cuda_stream"):
+        return int(s.cuda_stream) or None
+    return int(s) or None
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise FirOlsError(status, where)
+
+
+def fir_ols_plan(M: int, N: int, nchan: int = 1) -> int:
+    """Create a plan; returns the opaque handle as an integer."""
+    lib = load_library()
+    h = _vp()
+    _check(lib.fir_ols_plan(ctypes.byref(h), M, N, nchan), "fir_ols_plan")
+    return h.value
+
+
+def fir_ols_set_taps(plan: int, h, stream=None) -> None:
+    """Taps from host memory: real float32 or complex64 array of length M."""
+    lib = load_library()
+    h = np.asarray(h)
+    is_complex = np.iscomplexobj(h)
+    arr = np.ascontiguousarray(h, dtype=np.complex64 if is_complex else np.float32)
+    _check(lib.fir_ols_set_taps(plan, arr.ctypes.data, arr.size, int(is_complex), _stream(stream)),
+           "fir_ols_set_taps")
+
+
+def fir_ols_set_freq_response(plan: int, H, stream=None) -> None:
+    """Unscaled N-point response from host memory (complex64, bin 0 first)."""
+    lib = load_library()
+    arr = np.ascontiguousarray(np.asarray(H), dtype=np.complex64)
+    _check(lib.fir_ols_set_freq_response(plan, arr.ctypes.data, arr.size, _stream(stream)),
+           "fir_ols_set_freq_response")
+
+
+def fir_ols_execute(plan: int, x, y, nsamples: int, chan_stride: int, stream=None) -> None:
+    """Enqueue one call on device buffers x -> y ([nchan][chan_stride] complex64)."""
+    lib = load_library()
+    _check(lib.fir_ols_execute(plan, _ptr(x), _ptr(y), nsamples, chan_stride, _stream(stream)),
+           "fir_ols_execute")
+
+
+def fir_ols_set_state(plan: int, s0=None, stream=None) -> None:
+    lib = load_library()
+    _check(lib.fir_ols_set_state(plan, _ptr(s0), _stream(stream)), "fir_ols_set_state")
+
+
+def fir_ols_get_state(plan: int, out, stream=None) -> None:
+    lib = load_library()
+    _check(lib.fir_ols_get_state(plan, _ptr(out), _stream(stream)), "fir_ols_get_state")
+
+
+def fir_ols_destroy(plan: Optional[int]) -> None:
+    lib = load_library()
+    _check(lib.fir_ols_destroy(plan), "fir_ols_destroy")
+
+
+def fir_ols_block_length(plan: int) -> int:
+    lib = load_library()
+    L = lib.fir_ols_block_length(plan)
+    if L < 0:
+        raise FirOlsError(int(L), "fir_ols_block_length")
+    return int(L)
+
+
+def fir_ols_status_string(status: int) -> str:
+    return load_library().fir_ols_status_string(status).decode()
+
+
+class Plan:
+    """Owning wrapper of a plan that works on torch complex64 device tensors."""
+
+    def __init__(self, M: int, N: int, nchan: int = 1):
+        self.M, self.N, self.nchan = int(M), int(N), int(nchan)
+        self.handle = fir_ols_plan(self.M, self.N, self.nchan)
+        self.L = fir_ols_block_length(self.handle)
+
+    def set_taps(self, h, stream=None) -> "Plan":
+        fir_ols_set_taps(self.handle, h, stream)
+        return self
+
+    def set_freq_response(self, H, stream=None) -> "Plan":
+        fir_ols_set_freq_response(self.handle, H, stream)
+        return self
+
+    def _layout(self, x):
+        import torch
+        if x.dtype != torch.complex64 or not x.is_cuda:
+            raise FirOlsError(-1, "execute: x must be a complex64 device tensor")
+        if x.dim() == 1:
+            if self.nchan != 1:
+                raise FirOlsError(-1, "execute: x must be [nchan, n]")
+            return x.shape[0], max(x.shape[0], 1)
+        if x.dim() != 2 or x.shape[0] != self.nchan or (x.shape[1] > 1 and x.stride(1) != 1):
+            raise FirOlsError(-1, "execute: x must be [nchan, n] with unit inner stride")
+        return x.shape[1], max(x.stride(0), x.shape[1])
+
+    def execute(self, x, y=None, stream=None):
+        """Filter x (shape [n] or [nchan, n]); returns y (same shape/strides)."""
+        import torch
+        n, stride = self._layout(x)
+        if y is None:
+            y = torch.empty_strided(x.shape, x.stride(), dtype=x.dtype, device=x.device)
+        elif y.shape != x.shape or y.stride() != x.stride() or y.dtype != x.dtype:
+            raise FirOlsError(-1, "execute: y must match x in shape, strides and dtype")
+        fir_ols_execute(self.handle, x, y, n, stride, stream)
+        return y
+
+    def set_state(self, s0=None, stream=None) -> None:
+        fir_ols_set_state(self.handle, s0, stream)
+
+    def get_state(self, stream=None):
+        import torch
+        out = torch.empty((self.nchan, self.M - 1), dtype=torch.complex64, device="cuda")
+        fir_ols_get_state(self.handle, out, stream)
+        return out
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            fir_ols_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

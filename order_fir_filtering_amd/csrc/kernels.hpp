@@ -1,0 +1,46 @@
+// Internal interface between the C ABI (plan.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace firols {
+
+// Arguments of one overlap-save call over nchan channels.
+struct FusedArgs {
+    const float2 *x;        // [nchan][stride] input
+    float2 *y;              // [nchan][stride] output
+    const float2 *s0_old;   // [nchan][M-1] state read by this call (may be null if M == 1)
+    float2 *s0_new;         // [nchan][M-1] state written by this call
+    const float2 *H;        // N values, kernel order, scaled by 1/N
+    const float2 *tw;       // twiddle table of the transform
+    int64_t nsamples;       // samples per channel in this call (> 0)
+    int64_t stride;         // elements between channel starts
+    int64_t nblk;           // blocks per channel = ceil(nsamples / L)
+    int M;                  // taps
+    int L;                  // kept outputs per block
+    int nchan;
+};
+
+// Largest log2(N) the LDS-resident kernel covers.
+constexpr int kFusedMaxLogN = 14;
+constexpr int kMinLogN = 3;
+
+// Twiddle table size (float2) of the transform of size 2^logn.
+int twiddle_count(int logn);
+// Fill the twiddle table (host memory), computed in double, rounded to float.
+void build_twiddles(int logn, float2 *host_out);
+// perm[i]: the spectrum bin whose value the kernels expect at H[i].
+void build_h_permutation(int logn, int64_t *perm);
+
+// Filter one call (steps 3-5 of the method and the state carry).
+hipError_t launch_fused(int logn, const FusedArgs &a, hipStream_t stream);
+// H[i] = DFT_N(taps)[perm[i]] / N from N zero-padded complex taps.
+hipError_t launch_plan_taps(int logn, const float2 *taps_padded, float2 *H,
+                            const float2 *tw, hipStream_t stream);
+// dst[i] = src ? src[i] : 0 for i < count.
+hipError_t launch_copy(float2 *dst, const float2 *src, int64_t count,
+                       hipStream_t stream);
+
+}  // namespace firols

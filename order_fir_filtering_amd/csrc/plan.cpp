@@ -1,0 +1,227 @@
+// C ABI of the overlap-save FIR library: plans, filter set-up, execution
+// and state handling.  Argument meaning, ownership and error behaviour are
+// documented in include/firols.h.
+#include "firols.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <new>
+#include <vector>
+
+#include "kernels.hpp"
+
+struct fir_ols_plan_s {
+    int device = 0;
+    int logn = 0;
+    int64_t M = 0, N = 0, L = 0, nchan = 0;
+    float2 *H = nullptr;          // N values, kernel order, scaled by 1/N
+    float2 *tw = nullptr;         // twiddle table
+    float2 *taps = nullptr;       // N zero-padded taps, staging for set_taps
+    float2 *state[2] = {nullptr, nullptr};   // [nchan][M-1] each
+    int parity = 0;               // state[parity] is the current state
+    bool has_filter = false;
+};
+
+namespace {
+
+using firols::launch_copy;
+
+int ilog2_pow2(int64_t n) {
+    if (n <= 0 || (n & (n - 1))) return -1;
+    int l = 0;
+    while ((int64_t(1) << l) < n) ++l;
+    return l;
+}
+
+bool on_plan_device(const fir_ols_plan_s *p) {
+    int d = -1;
+    return hipGetDevice(&d) == hipSuccess && d == p->device;
+}
+
+void release(fir_ols_plan_s *p) {
+    hipFree(p->H);
+    hipFree(p->tw);
+    hipFree(p->taps);
+    hipFree(p->state[0]);
+    hipFree(p->state[1]);
+    delete p;
+}
+
+int64_t state_len(const fir_ols_plan_s *p) { return p->nchan * (p->M - 1); }
+
+}  // namespace
+
+extern "C" {
+
+int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
+    if (!out) return FIR_OLS_ERR_INVALID_ARG;
+    *out = nullptr;
+    const int logn = ilog2_pow2(N);
+    if (logn < 0 || M < 1 || M > N || nchan < 1) return FIR_OLS_ERR_INVALID_ARG;
+    if (logn < firols::kMinLogN || logn > firols::kFusedMaxLogN) return FIR_OLS_ERR_UNSUPPORTED;
+    if (nchan > (int64_t)1 << 30 || (M - 1) * nchan > ((int64_t)1 << 40))
+        return FIR_OLS_ERR_UNSUPPORTED;
+
+    fir_ols_plan_s *p = new (std::nothrow) fir_ols_plan_s;
+    if (!p) return FIR_OLS_ERR_OOM;
+    if (hipGetDevice(&p->device) != hipSuccess) {
+        delete p;
+        return FIR_OLS_ERR_HIP;
+    }
+    p->logn = logn;
+    p->M = M;
+    p->N = N;
+    p->L = N - M + 1;
+    p->nchan = nchan;
+
+    const int ntw = firols::twiddle_count(logn);
+    const size_t sbytes = (size_t)state_len(p) * sizeof(float2);
+    bool ok = hipMalloc(&p->H, N * sizeof(float2)) == hipSuccess &&
+              hipMalloc(&p->tw, (size_t)(ntw > 0 ? ntw : 1) * sizeof(float2)) == hipSuccess &&
+              hipMalloc(&p->taps, N * sizeof(float2)) == hipSuccess;
+    if (ok && sbytes) {
+        ok = hipMalloc(&p->state[0], sbytes) == hipSuccess &&
+             hipMalloc(&p->state[1], sbytes) == hipSuccess;
+    }
+    if (!ok) {
+        (void)hipGetLastError();
+        release(p);
+        return FIR_OLS_ERR_OOM;
+    }
+
+    std::vector<float2> tw((size_t)(ntw > 0 ? ntw : 1), make_float2(1.f, 0.f));
+    firols::build_twiddles(logn, tw.data());
+    hipError_t e = hipMemcpy(p->tw, tw.data(), tw.size() * sizeof(float2), hipMemcpyHostToDevice);
+    if (e == hipSuccess && sbytes) e = launch_copy(p->state[0], nullptr, state_len(p), nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        release(p);
+        return FIR_OLS_ERR_HIP;
+    }
+    *out = p;
+    return FIR_OLS_OK;
+}
+
+int fir_ols_set_taps(fir_ols_plan_t p, const float *h_host, int64_t M, int is_complex,
+                     void *stream) {
+    if (!p || !h_host || M != p->M) return FIR_OLS_ERR_INVALID_ARG;
+    if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
+    std::vector<float2> padded((size_t)p->N, make_float2(0.f, 0.f));
+    for (int64_t m = 0; m < M; ++m)
+        padded[m] = is_complex ? make_float2(h_host[2 * m], h_host[2 * m + 1])
+                               : make_float2(h_host[m], 0.f);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(p->taps, padded.data(), p->N * sizeof(float2),
+                                  hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = firols::launch_plan_taps(p->logn, p->taps, p->H, p->tw, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return FIR_OLS_ERR_HIP;
+    p->has_filter = true;
+    return FIR_OLS_OK;
+}
+
+int fir_ols_set_freq_response(fir_ols_plan_t p, const float *H_host, int64_t N, void *stream) {
+    if (!p || !H_host || N != p->N) return FIR_OLS_ERR_INVALID_ARG;
+    if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
+    std::vector<int64_t> perm((size_t)N);
+    firols::build_h_permutation(p->logn, perm.data());
+    const float scale = 1.0f / (float)N;   // exact: N is a power of two
+    std::vector<float2> Hk((size_t)N);
+    for (int64_t i = 0; i < N; ++i) {
+        const int64_t b = perm[i];
+        Hk[i] = make_float2(H_host[2 * b] * scale, H_host[2 * b + 1] * scale);
+    }
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(p->H, Hk.data(), N * sizeof(float2), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return FIR_OLS_ERR_HIP;
+    p->has_filter = true;
+    return FIR_OLS_OK;
+}
+
+int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev, int64_t nsamples,
+                    int64_t chan_stride, void *stream) {
+    if (!p || nsamples < 0) return FIR_OLS_ERR_INVALID_ARG;
+    if (!p->has_filter) return FIR_OLS_ERR_NO_FILTER;
+    if (nsamples == 0) return FIR_OLS_OK;
+    if (!x_dev || !y_dev || chan_stride < nsamples) return FIR_OLS_ERR_INVALID_ARG;
+    if (((uintptr_t)x_dev | (uintptr_t)y_dev) & 7) return FIR_OLS_ERR_ALIGN;
+    if (chan_stride > ((int64_t)1 << 50) / p->nchan) return FIR_OLS_ERR_INVALID_ARG;
+    const int64_t span = ((p->nchan - 1) * chan_stride + nsamples) * (int64_t)sizeof(float2);
+    const uintptr_t xa = (uintptr_t)x_dev, ya = (uintptr_t)y_dev;
+    if (xa < ya + (uintptr_t)span && ya < xa + (uintptr_t)span) return FIR_OLS_ERR_ALIAS;
+    if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
+
+    firols::FusedArgs a;
+    a.x = (const float2 *)x_dev;
+    a.y = (float2 *)y_dev;
+    a.s0_old = p->state[p->parity];
+    a.s0_new = p->state[p->parity ^ 1];
+    a.H = p->H;
+    a.tw = p->tw;
+    a.nsamples = nsamples;
+    a.stride = chan_stride;
+    a.nblk = (nsamples + p->L - 1) / p->L;
+    a.M = (int)p->M;
+    a.L = (int)p->L;
+    a.nchan = (int)p->nchan;
+    hipError_t e = firols::launch_fused(p->logn, a, (hipStream_t)stream);
+    if (e != hipSuccess) return FIR_OLS_ERR_HIP;
+    if (p->M > 1) p->parity ^= 1;
+    return FIR_OLS_OK;
+}
+
+int fir_ols_set_state(fir_ols_plan_t p, const void *s0_dev, void *stream) {
+    if (!p) return FIR_OLS_ERR_INVALID_ARG;
+    if (p->M == 1) return FIR_OLS_OK;
+    if (s0_dev && ((uintptr_t)s0_dev & 7)) return FIR_OLS_ERR_ALIGN;
+    if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
+    hipError_t e = launch_copy(p->state[p->parity], (const float2 *)s0_dev, state_len(p),
+                               (hipStream_t)stream);
+    return e == hipSuccess ? FIR_OLS_OK : FIR_OLS_ERR_HIP;
+}
+
+int fir_ols_get_state(fir_ols_plan_t p, void *s0_out_dev, void *stream) {
+    if (!p) return FIR_OLS_ERR_INVALID_ARG;
+    if (p->M == 1) return FIR_OLS_OK;
+    if (!s0_out_dev) return FIR_OLS_ERR_INVALID_ARG;
+    if ((uintptr_t)s0_out_dev & 7) return FIR_OLS_ERR_ALIGN;
+    if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
+    hipError_t e = launch_copy((float2 *)s0_out_dev, p->state[p->parity], state_len(p),
+                               (hipStream_t)stream);
+    return e == hipSuccess ? FIR_OLS_OK : FIR_OLS_ERR_HIP;
+}
+
+int fir_ols_destroy(fir_ols_plan_t p) {
+    if (!p) return FIR_OLS_OK;
+    const int dev = p->device;
+    int old = -1;
+    hipError_t e = hipGetDevice(&old);
+    if (e == hipSuccess && old != dev) e = hipSetDevice(dev);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    release(p);
+    if (old >= 0 && old != dev) (void)hipSetDevice(old);
+    return e == hipSuccess ? FIR_OLS_OK : FIR_OLS_ERR_HIP;
+}
+
+int64_t fir_ols_block_length(fir_ols_plan_t p) {
+    return p ? p->L : (int64_t)FIR_OLS_ERR_INVALID_ARG;
+}
+
+const char *fir_ols_status_string(int status) {
+    switch (status) {
+        case FIR_OLS_OK: return "ok";
+        case FIR_OLS_ERR_INVALID_ARG: return "invalid argument";
+        case FIR_OLS_ERR_UNSUPPORTED: return "unsupported size";
+        case FIR_OLS_ERR_NO_FILTER: return "no filter set";
+        case FIR_OLS_ERR_ALIAS: return "input and output overlap";
+        case FIR_OLS_ERR_ALIGN: return "pointer not 8-byte aligned";
+        case FIR_OLS_ERR_OOM: return "device allocation failed";
+        case FIR_OLS_ERR_HIP: return "HIP runtime error";
+        case FIR_OLS_ERR_DEVICE: return "current device is not the plan's device";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+"""The C ABI library loads and exports what include/firols.h declares (CPU).
+
+Only argument checks that return before any HIP call are exercised here.
+"""
+import os
+import re
+
+import pytest
+
+import order_fir_filtering_amd as fo
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "firols.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fir_ols_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fo.LIBRARY_PATH):
+        from order_fir_filtering_amd.build import build
+        build()
+    return fo.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for need in ("fir_ols_plan", "fir_ols_set_taps", "fir_ols_set_freq_response",
+                 "fir_ols_execute", "fir_ols_destroy"):
+        assert need in names
+    assert sorted(fo.EXPORTED) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert fo.fir_ols_status_string(0) == "ok"
+    assert "overlap" in fo.fir_ols_status_string(-4)
+    assert fo.fir_ols_status_string(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("M,N,nchan,status", [
+    (5, 100, 1, -1),        # N not a power of two
+    (0, 64, 1, -1),         # M < 1
+    (65, 64, 1, -1),        # M > N
+    (5, 64, 0, -1),         # no channels
+    (3, 4, 1, -2),          # N below the smallest kernel
+    (3, 1 << 17, 1, -2),    # N above the largest kernel
+])
+def test_plan_argument_checks(lib, M, N, nchan, status):
+    with pytest.raises(fo.FirOlsError) as e:
+        fo.fir_ols_plan(M, N, nchan)
+    assert e.value.status == status
+
+
+def test_null_handles(lib):
+    assert lib.fir_ols_destroy(None) == 0
+    assert lib.fir_ols_block_length(None) == -1
+    assert lib.fir_ols_execute(None, None, None, 10, 10, None) == -1
+    assert lib.fir_ols_set_taps(None, None, 3, 0, None) == -1
+    assert lib.fir_ols_set_freq_response(None, None, 8, None) == -1
+    assert lib.fir_ols_set_state(None, None, None) == -1
+    assert lib.fir_ols_get_state(None, None, None) == -1
+    assert lib.fir_ols_plan(None, 3, 8, 1) == -1
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(fo.FirOlsError):
+        fo.load_library(str(tmp_path / "libfirols.so"))
