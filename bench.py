@@ -1,0 +1,429 @@
+"""Benchmark of overlap-save FIR filtering on one MI355X.
+
+One step = one pass of the whole hot path over one batch of the workload:
+for the default workload (M=1025 windowed-sinc taps, N=4096, L=3072) that
+is 4 sequential calls of 786,432 complex64 samples with the state carried
+between them.  Inputs are resident in device memory before timing; the
+step rotates through enough input/output buffer sets to exceed the 256 MB
+last-level cache, so every step streams from HBM.
+
+Prints one JSON line: Msamples/s of filtered output, the roofline of the
+dominant kernel (algorithmic 16 B per sample: one complex64 read and one
+write, timed with HIP events around each launch on the launch stream), a
+copy reference, a parity check of one step against the float64 oracle and
+the oracle's own CPU throughput (reported baseline, not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, AMD published figure
+BYTES_PER_SAMPLE = 16             # complex64 in + complex64 out
+LLC_BYTES = 256 << 20             # MI355X Infinity Cache
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=0,
+                    help="timed steps (default: about one second of steps, at least 50)")
+    ap.add_argument("--warmup", type=int, default=-1,
+                    help="untimed warm-up steps (default: about one second of steps)")
+    ap.add_argument("--workload", default="cfg2",
+                    help="cfg1..cfg5 (default cfg2: M=1025, N=4096, 4 calls)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write a profiles/ summary of a rocprofv3 --kernel-trace --stats "
+                         "CSV run of this script, then exit")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="calibrate FETCH_SIZE / WRITE_SIZE runs of this script against "
+                         "the copy kernel, write profiles/ summaries, then exit")
+    ap.add_argument("--command", default="", help="command line recorded in the summary")
+    return ap.parse_args()
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return list(csv.DictReader(open(files[0])))
+
+
+def _short(name: str) -> str:
+    return name.split("(")[0].replace("void ", "")[:80]
+
+
+def summarize_trace(args):
+    """profiles/<kernel>_<workload>_kernel_trace.md from run_kernel_stats.csv."""
+    rows = _csv_rows(args.summarize_trace, "kernel_stats.csv")
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    top = _short(rows[0]["Name"]).split("::")[-1].replace("<", "_").replace(">", "")
+    out = os.path.join(ROOT, "profiles", f"{top}_{args.workload}_kernel_trace.md")
+    lines = [f"# Kernel trace: {args.workload} ({WORKLOAD_NOTE.get(args.workload, '')})", "",
+             "Command (run from /tmp on the GPU box):", "", "```", args.command, "```", "",
+             f"Kernel source hash: `{kernel_source_hash()}`", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in rows[:8]:
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.3f} | "
+                     f"{float(r['MinNs'])/1e3:.3f} | {float(r['MaxNs'])/1e3:.3f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(out)
+
+
+def summarize_pmc(args):
+    """Calibrated HBM traffic of the filtering kernel from two counter runs."""
+    import workloads as W
+    w = W.WORKLOADS[args.workload]
+    copy_kib = w.nchan * w.samples * 8 / 1024.0   # bytes read (= written) by the copy kernel
+    res = {}
+    for counter, d in (("FETCH_SIZE", args.summarize_pmc[0]), ("WRITE_SIZE", args.summarize_pmc[1])):
+        per = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        ols = {k: v for k, v in per.items() if "ols_" in k and "plan_taps" not in k}
+        cal = [v for k, v in per.items() if "neg" in k]
+        if not ols or not cal:
+            raise SystemExit(f"{counter}: filtering or copy kernel missing in {d}")
+        cal_mean = float(np.mean(cal[0]))
+        scale = copy_kib / cal_mean
+        res[counter] = {"scale": scale, "copy_kib_counted": cal_mean, "copy_kib_true": copy_kib,
+                        "kernels": {_short(k): float(np.mean(v)) for k, v in ols.items()}}
+    kernels = res["FETCH_SIZE"]["kernels"]
+    calls = len(w.calls)
+    step_bytes = 0.0
+    for k in kernels:
+        step_bytes += (kernels[k] * res["FETCH_SIZE"]["scale"]
+                       + res["WRITE_SIZE"]["kernels"].get(k, 0.0) * res["WRITE_SIZE"]["scale"]) * 1024
+    # per launch of the filtering call (all kernels of one call)
+    per_launch = step_bytes  # counters are per dispatch; one dispatch per call
+    alg = w.nchan * w.samples / calls * BYTES_PER_SAMPLE
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        db = json.load(open(path))
+    except (OSError, ValueError):
+        db = {}
+    db[args.workload] = {"bytes_per_launch": round(per_launch), "algorithmic_bytes_per_launch": alg,
+                         "ratio": round(per_launch / alg, 4), "source_hash": kernel_source_hash(),
+                         "fetch_scale": round(res["FETCH_SIZE"]["scale"], 4),
+                         "write_scale": round(res["WRITE_SIZE"]["scale"], 4)}
+    json.dump(db, open(path, "w"), indent=1, sort_keys=True)
+    top = sorted(kernels)[0].split("::")[-1].replace("<", "_").replace(">", "")
+    out = os.path.join(ROOT, "profiles", f"{top}_{args.workload}_hbm_traffic.md")
+    lines = [f"# HBM traffic: {args.workload} ({WORKLOAD_NOTE.get(args.workload, '')})", "",
+             "Two counter runs of the same command, one per counter (run from /tmp on the GPU box):",
+             "", "```", args.command, "```", "",
+             f"Kernel source hash: `{kernel_source_hash()}`", "",
+             "The counters are read per dispatch in KiB.  Each is scaled by the ratio of the true "
+             "bytes to the counted KiB of the elementwise copy kernel in the same run "
+             f"(`torch.neg` over {copy_kib:.0f} KiB read and written).", "",
+             "| counter | copy kernel counted (KiB) | true (KiB) | scale |", "|---|---|---|---|"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        lines.append(f"| {c} | {res[c]['copy_kib_counted']:.1f} | {copy_kib:.1f} | {res[c]['scale']:.4f} |")
+    lines += ["", "| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled bytes per dispatch |",
+              "|---|---|---|---|"]
+    for k in kernels:
+        fb = kernels[k] * res["FETCH_SIZE"]["scale"] * 1024
+        wb = res["WRITE_SIZE"]["kernels"].get(k, 0.0) * res["WRITE_SIZE"]["scale"] * 1024
+        lines.append(f"| `{k}` | {kernels[k]:.1f} | {res['WRITE_SIZE']['kernels'].get(k, 0.0):.1f} | "
+                     f"{fb + wb:.4g} |")
+    lines += ["", f"Algorithmic bytes per call (16 B per output sample): {alg:.4g}.  "
+              f"Measured / algorithmic: {per_launch / alg:.3f}."]
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(out)
+
+
+def cpu_baseline(inp, seconds_budget: float = 20.0):
+    """Time the float64 oracle on the host cores on a bounded output sample.
+
+    Returns the baseline record and the oracle outputs it computed (all
+    outputs when the whole workload fits the budget, else None).
+    """
+    import oracle
+    w = inp.workload
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = max(1, min(int(threads), 64))
+    total = w.nchan * w.samples
+    # calibrate on a small sample, then size the timed sample to the budget
+    n_cal = 4096
+    t0 = time.perf_counter()
+    oracle.fir_direct(inp.h_ref, inp.x[0], inp.s0[0], idx=np.arange(min(n_cal, w.samples)),
+                      threads=threads)
+    per = (time.perf_counter() - t0) / min(n_cal, w.samples)
+    want = int(min(total, max(n_cal, seconds_budget / max(per, 1e-12))))
+    ref = None
+    if want >= total:
+        sample = f"all {total} outputs of the workload"
+        reps, dt = 0, 0.0
+        while reps < 20 and (reps == 0 or dt < 2.0):
+            t0 = time.perf_counter()
+            ref = oracle.fir_direct_multi(inp.h_ref, inp.x, inp.s0, threads=threads)
+            dt += time.perf_counter() - t0
+            reps += 1
+        count = total * reps
+        if reps > 1:
+            sample += f", computed {reps} times"
+    else:
+        per_chan = max(1, want // w.nchan)
+        idx = np.linspace(0, w.samples - 1, per_chan).astype(np.int64)
+        sample = (f"{per_chan} evenly spaced outputs per channel x {w.nchan} channel(s) "
+                  f"of {total}")
+        t0 = time.perf_counter()
+        oracle.fir_direct_multi(inp.h_ref, inp.x, inp.s0, idx=idx, threads=threads)
+        dt = time.perf_counter() - t0
+        count = per_chan * w.nchan
+    # the same oracle on one thread, on a sample of about two seconds
+    n1 = int(max(256, min(w.samples, 2.0 / max(per * threads, 1e-12))))
+    idx1 = np.linspace(0, w.samples - 1, n1).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.fir_direct(inp.h_ref, inp.x[0], inp.s0[0], idx=idx1, threads=1)
+    dt1 = time.perf_counter() - t0
+    return {"value": count / dt / 1e6, "unit": "Msamples/s", "cores": threads,
+            "kind": "oracle", "sample": sample, "seconds": round(dt, 3),
+            "single_thread_value": n1 / dt1 / 1e6,
+            "single_thread_sample": f"{n1} evenly spaced outputs of channel 0"}, ref
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    d = os.path.join(ROOT, "order_fir_filtering_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken with the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path)).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+WORKLOAD_NOTE = {
+    "cfg1": "M=65, N=256, 12288 samples",
+    "cfg2": "M=1025, N=4096, 4 calls of 786432 samples",
+    "cfg3": "M=8193, N=32768, 50331648 samples",
+    "cfg4": "M=16385, N=65536 via H, 251658240 samples",
+    "cfg5": "M=257, N=1024, 1024 channels x 65536 samples",
+}
+
+
+def main():
+    args = parse()
+    if args.summarize_trace:
+        summarize_trace(args)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import order_fir_filtering_amd as fo
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    fo.load_library()
+
+    inp = W.make_inputs(args.workload)
+    w = inp.workload
+    samples_per_step = w.nchan * w.samples
+    step_bytes = samples_per_step * BYTES_PER_SAMPLE
+    nsets = max(1, min(64, -(-2 * LLC_BYTES // step_bytes)))
+    print(f"# workload {w.key}: {w.description}; {nsets} buffer set(s)", file=sys.stderr, flush=True)
+
+    x_host = torch.from_numpy(inp.x)
+    xs = [x_host.to(dev) for _ in range(nsets)]
+    ys = [torch.empty_like(xs[0]) for _ in range(nsets)]
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    plan = fo.Plan(w.M, w.N, w.nchan)
+    if inp.H is not None:
+        plan.set_freq_response(inp.H)
+    else:
+        plan.set_taps(inp.taps)
+    s0_dev = torch.from_numpy(inp.s0).to(dev)
+    plan.set_state(s0_dev)
+    item = 8
+    stride = w.samples
+
+    def step(k, events=None):
+        x, y = xs[k % nsets], ys[k % nsets]
+        pos = 0
+        for c in w.calls:
+            if events is not None:
+                events[0].record(stream)
+            fo.fir_ols_execute(plan.handle, x.data_ptr() + pos * item,
+                               y.data_ptr() + pos * item, c, stride, sptr)
+            if events is not None:
+                events[1].record(stream)
+                events = events[2:]
+            pos += c
+
+    # parity of one step against the oracle (fresh state, before timing)
+    parity = None
+    ref = None
+    base = None
+    if not args.no_cpu_baseline:
+        base, ref = cpu_baseline(inp)
+    if not args.no_parity:
+        import oracle
+        plan.set_state(s0_dev)
+        step(0)
+        torch.cuda.synchronize()
+        y0 = ys[0].cpu().numpy()
+        if ref is not None and ref.shape == y0.shape:
+            yref, idx = ref, None
+        else:
+            idx = W.sample_indices(7, w.samples, 4096)
+            yref = oracle.fir_direct_multi(inp.h_ref, inp.x, inp.s0, idx=idx,
+                                           threads=len(os.sched_getaffinity(0)))
+            y0 = y0[:, idx]
+        err = float(np.abs(y0.astype(np.complex128) - yref).max())
+        bound = oracle.parity_bound(inp.h_ref, inp.x, inp.s0)
+        parity = {"max_abs_err": err, "bound": bound, "ok": err <= bound,
+                  "outputs_checked": int(yref.size)}
+
+    # size the default warm-up and step counts from a short probe, so the
+    # clocks have settled before timing (a few ms of warm-up is not enough)
+    probe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step(0)
+    probe[0].record(stream)
+    for k in range(5):
+        step(k)
+    probe[1].record(stream)
+    torch.cuda.synchronize()
+    est_ms = max(probe[0].elapsed_time(probe[1]) / 5, 1e-3)
+    if args.warmup < 0:
+        args.warmup = max(20, int(1000.0 / est_ms))
+    if args.steps <= 0:
+        args.steps = max(50, int(1000.0 / est_ms))
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    ncalls = len(w.calls)
+    # timed region: exactly K steps, nothing else on the stream
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(k)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    value = samples_per_step / (ms_per_step * 1e-3) / 1e6
+
+    # per-launch durations of the filtering kernel: HIP events around each
+    # launch on the launch stream, over another K steps
+    ksteps = min(args.steps, 200)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * ncalls * ksteps)]
+    torch.cuda.synchronize()
+    for k in range(ksteps):
+        step(k, evs[2 * ncalls * k: 2 * ncalls * (k + 1)])
+    torch.cuda.synchronize()
+    launch_ms = [evs[2 * j].elapsed_time(evs[2 * j + 1]) for j in range(ncalls * ksteps)]
+
+    # dominant kernel: the filtering kernel; algorithmic bytes per launch
+    per_launch_samples = [w.nchan * c for c in w.calls] * ksteps
+    kern_ms = float(np.mean(launch_ms))
+    kern_bytes = float(np.mean(per_launch_samples)) * BYTES_PER_SAMPLE
+    achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
+
+    # copy reference: the same bytes through a plain elementwise kernel (one
+    # read and one write per element); also the calibration dispatch for
+    # the FETCH_SIZE / WRITE_SIZE counters
+    fx = [x.view(torch.float32).view(-1) for x in xs]
+    fy = [y.view(torch.float32).view(-1) for y in ys]
+    for r in range(3):
+        torch.neg(fx[r % nsets], out=fy[r % nsets])
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    reps = max(5, min(200, int(200.0 / max(est_ms, 1e-3))))
+    torch.cuda.synchronize()
+    c0.record(stream)
+    for r in range(reps):
+        torch.neg(fx[r % nsets], out=fy[r % nsets])
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = reps * 2 * fx[0].numel() * 4 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+
+    plan.close()
+    out = {
+        "metric": "filtered output Msamples/s (complex fp32) and % of HBM roof, per (M,N)",
+        "value": round(value, 1),
+        "unit": "Msamples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.key}: {w.description}",
+            "M": w.M, "N": w.N, "L": w.L, "nchan": w.nchan,
+            "calls_per_step": ncalls, "samples_per_step": samples_per_step,
+            "buffer_sets": nsets,
+            "hbm_roof_fraction": round(value * 1e6 * BYTES_PER_SAMPLE / (HBM_PEAK_GBPS * 1e9), 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"ols_fused_kernel<{int(np.log2(w.N))}>",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(w.key),
+            "avg_launch_us": round(kern_ms * 1e3, 3),
+            "kernel_source_hash": kernel_source_hash(),
+            "algorithmic_bytes_per_launch": int(kern_bytes),
+        },
+        "copy_reference_GBps": round(copy_gbps, 1),
+        "parity": parity,
+        "cpu_baseline": base,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,10 +1,10 @@
 // Compile-time geometry of the LDS-resident overlap-save kernel.
 //
 // One N-point block is transformed by TB = N / P threads that each hold P
-// complex points in registers (P = 16, or N itself when N < 16).  The
+// complex points in registers (P = 16 by default, or N itself when N < 16).  The
 // transform is an in-place mixed-radix decimation-in-frequency FFT with
-// radices R[0..npass-1] (one radix 2/4/8 pass first when log2(N) is not a
-// multiple of 4, then radix-16 passes).  Pass s works at stride
+// radices R[0..npass-1] (one smaller radix pass first when log2(N) is not a
+// multiple of log2(P), then radix-P passes).  Pass s works at stride
 // S[s] = N / (R[0] * ... * R[s]):
 //
 //   virtual thread v in [0, N/R[s]),  K = v / S[s],  t = v % S[s]
@@ -25,31 +25,31 @@ namespace firols {
 constexpr int kMaxPass = 8;
 
 struct Geo {
-    int logn, N, P, TB, npass;
+    int logn, logp, N, P, TB, npass;
     int R[kMaxPass];
     int S[kMaxPass];
     int twoff[kMaxPass + 1];   // start of pass s's twiddles in the table
     int lds_stride;            // padded LDS slots of one block (float2)
 };
 
-// LDS slot of position p: one pad slot after every 16 keeps the strided
-// accesses of the late passes off a single bank.
-constexpr int lds_pad(int p) { return p + (p >> 4); }
+// A geometry id packs log2(N) (low byte) and, optionally, log2(P) (next
+// byte; 0 selects the default P = 16, or N when N < 16).
+constexpr int geo_id(int logn, int logp = 0) { return logn | (logp << 8); }
 
-constexpr Geo make_geo(int logn) {
+constexpr Geo make_geo(int gid) {
     Geo g{};
+    const int logn = gid & 0xff;
+    int logp = gid >> 8;
+    if (logp == 0) logp = logn >= 4 ? 4 : logn;
     g.logn = logn;
+    g.logp = logp;
     g.N = 1 << logn;
-    g.P = logn >= 4 ? 16 : g.N;
+    g.P = 1 << logp;
     g.TB = g.N / g.P;
     int np = 0;
-    if (logn < 4) {
-        g.R[np++] = g.N;
-    } else {
-        int rem = logn % 4;
-        if (rem) g.R[np++] = 1 << rem;
-        for (int i = 0; i < logn / 4; ++i) g.R[np++] = 16;
-    }
+    const int rem = logn % logp;
+    if (rem) g.R[np++] = 1 << rem;
+    for (int i = 0; i < logn / logp; ++i) g.R[np++] = g.P;
     g.npass = np;
     int S = g.N;
     g.twoff[0] = 0;
@@ -58,13 +58,17 @@ constexpr Geo make_geo(int logn) {
         g.S[s] = S;
         g.twoff[s + 1] = g.twoff[s] + S * (g.R[s] - 1);
     }
-    g.lds_stride = lds_pad(g.N);
+    g.lds_stride = g.N + (g.N >> logp);
     return g;
 }
 
+// LDS slot of position p: one pad slot after every P positions keeps the
+// strided accesses of the late passes off a single bank.
+constexpr int lds_pad(const Geo &g, int p) { return p + (p >> g.logp); }
+
 // Blocks per workgroup: small transforms share a 256-lane workgroup.
-constexpr int blocks_per_wg(int logn) {
-    int tb = make_geo(logn).TB;
+constexpr int blocks_per_wg(int gid) {
+    int tb = make_geo(gid).TB;
     return tb >= 256 ? 1 : 256 / tb;
 }
 

@@ -34,8 +34,12 @@ void build_twiddles(int logn, float2 *host_out);
 // perm[i]: the spectrum bin whose value the kernels expect at H[i].
 void build_h_permutation(int logn, int64_t *perm);
 
+// Workgroups of the filtering kernel that fit on the device at once
+// (resident workgroups per CU times CUs); the kernel is persistent and
+// never launches more.
+int fused_max_groups(int logn, int device);
 // Filter one call (steps 3-5 of the method and the state carry).
-hipError_t launch_fused(int logn, const FusedArgs &a, hipStream_t stream);
+hipError_t launch_fused(int logn, const FusedArgs &a, int max_groups, hipStream_t stream);
 // H[i] = DFT_N(taps)[perm[i]] / N from N zero-padded complex taps.
 hipError_t launch_plan_taps(int logn, const float2 *taps_padded, float2 *H,
                             const float2 *tw, hipStream_t stream);

@@ -15,80 +15,133 @@
 
 namespace firols {
 
-template <int LOGN>
+template <int GID>
 struct FusedCfg {
-    static constexpr Geo G = make_geo(LOGN);
-    static constexpr int BPW = blocks_per_wg(LOGN);
+    static constexpr Geo G = make_geo(GID);
+    static constexpr int BPW = blocks_per_wg(GID);
     static constexpr int WG = G.TB * BPW;
     static constexpr int LDSN = G.npass > 1 ? G.lds_stride * BPW : 1;
+    // Twiddles and H stay in registers for the whole kernel when the VGPR
+    // budget allows it (the workgroup runs many blocks, and a thread always
+    // holds the same positions of each block).
+    static constexpr bool REGS = G.logn <= 12;
+    // Buffer-descriptor I/O needs whole waves per block; at 1024 threads per
+    // block (128 VGPRs) its extra offsets would spill, so that size keeps
+    // pointer I/O.
+    static constexpr bool WAVE_IO = G.TB >= 64 && G.TB < 1024;
 };
 
 // Forward passes with LDS exchanges between them.
-template <int LOGN>
-__device__ __forceinline__ void forward_all(int tb, float2 (&a)[make_geo(LOGN).P],
-                                            float2 *lds, const float2 *__restrict__ tw) {
-    constexpr Geo G = make_geo(LOGN);
+template <int GID, class TW>
+__device__ __forceinline__ void forward_all(int tb, float2 (&a)[make_geo(GID).P],
+                                            float2 *lds, const TW &tw) {
+    constexpr Geo G = make_geo(GID);
     static_for<0, G.npass>([&](auto Sx) {
         constexpr int s = decltype(Sx)::value;
         if constexpr (s > 0) {
             __syncthreads();
-            lds_put<LOGN, s - 1>(tb, a, lds);
+            lds_put<GID, s - 1>(tb, a, lds);
             __syncthreads();
-            lds_get<LOGN, s>(tb, a, lds);
+            lds_get<GID, s>(tb, a, lds);
         }
-        fwd_pass<LOGN, s>(tb, a, tw);
+        fwd_pass<GID, s>(a, tw);
     });
 }
 
 // Inverse passes in reverse order with LDS exchanges between them.
-template <int LOGN>
-__device__ __forceinline__ void inverse_all(int tb, float2 (&a)[make_geo(LOGN).P],
-                                            float2 *lds, const float2 *__restrict__ tw) {
-    constexpr Geo G = make_geo(LOGN);
+template <int GID, class TW>
+__device__ __forceinline__ void inverse_all(int tb, float2 (&a)[make_geo(GID).P],
+                                            float2 *lds, const TW &tw) {
+    constexpr Geo G = make_geo(GID);
     static_for<0, G.npass>([&](auto Ix) {
         constexpr int s = G.npass - 1 - decltype(Ix)::value;
         if constexpr (s < G.npass - 1) {
             __syncthreads();
-            lds_put<LOGN, s + 1>(tb, a, lds);
+            lds_put<GID, s + 1>(tb, a, lds);
             __syncthreads();
-            lds_get<LOGN, s>(tb, a, lds);
+            lds_get<GID, s>(tb, a, lds);
         }
-        inv_pass<LOGN, s>(tb, a, tw);
+        inv_pass<GID, s>(a, tw);
     });
 }
 
-template <int LOGN>
-__global__ __launch_bounds__(FusedCfg<LOGN>::WG) void ols_fused_kernel(FusedArgs A) {
-    using C = FusedCfg<LOGN>;
-    constexpr Geo G = make_geo(LOGN);
-    __shared__ float2 lds[C::LDSN];
+// Work unit (BPW consecutive blocks) of the it-th iteration of workgroup w,
+// or -1 when the workgroup is done.  Workgroups are dispatched round-robin
+// over the 8 XCDs (w % 8); each XCD takes one contiguous eighth of the
+// units, so neighbouring blocks, whose gathers overlap by M-1 samples, run
+// on the same XCD and share its L2.
+__device__ __forceinline__ int64_t unit_of(int64_t units, int w, int G, int64_t it) {
+    if ((G & 7) == 0) {
+        const int per = G >> 3;
+        const int64_t chunk = (units + 7) >> 3;
+        const int64_t lo = (int64_t)(w & 7) * chunk;
+        const int64_t u = lo + (w >> 3) + it * per;
+        const int64_t hi = lo + chunk < units ? lo + chunk : units;
+        return u < hi ? u : -1;
+    }
+    const int64_t u = w + it * G;
+    return u < units ? u : -1;
+}
 
-    const int tid = threadIdx.x;
-    const int sub = tid / G.TB;
-    const int tb = tid - sub * G.TB;
-    float2 *my = lds + sub * G.lds_stride;
+// Raw buffer access (gfx9 family): a 128-bit descriptor holds a base
+// address and a byte size; a load whose 32-bit offset is at or past the
+// size returns zero and such a store is dropped.  The kernels use this to
+// zero-fill positions outside the input and to drop the M-1 discarded and
+// the past-the-end outputs without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ float2 buf_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ void buf_store(float2 v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(decltype(
+        __builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, voff, 0, 0);
+}
 
-    const int64_t total = A.nblk * A.nchan;
-    const int64_t gb = (int64_t)blockIdx.x * C::BPW + sub;
-    const bool active = gb < total;
+// Kept outputs of a block and the state carry.
+template <int GID>
+__device__ __forceinline__ void carry_state(const FusedArgs &A, int64_t c, int tb,
+                                            const float2 *__restrict__ xc,
+                                            const float2 *__restrict__ sc) {
+    constexpr Geo G = make_geo(GID);
+    const int Mm1 = A.M - 1;
+    float2 *__restrict__ sn = A.s0_new + c * Mm1;
+    for (int r = tb; r < Mm1; r += G.TB) {
+        const int64_t g = A.nsamples - Mm1 + r;
+        sn[r] = g >= 0 ? xc[g] : sc[Mm1 + g];
+    }
+}
+
+// One block: gather (step 3), FFT / product / inverse FFT (step 4), store
+// of the kept points (step 5), and the state carry of the channel's last
+// block.  Inactive threads (padding sub-blocks) take part in the barriers.
+// This form serves blocks smaller than a wavefront (several blocks share a
+// wave), with plain pointer accesses.
+template <int GID, class TW, class HP>
+__device__ __forceinline__ void filter_block(const FusedArgs &A, int64_t gb, bool active, int tb,
+                                             float2 *my, const TW &tw, const HP &hp) {
+    constexpr Geo G = make_geo(GID);
     const int64_t c = active ? gb / A.nblk : 0;
     const int64_t i = active ? gb - c * A.nblk : 0;
     const int Mm1 = A.M - 1;
     const float2 *__restrict__ xc = A.x + c * A.stride;
     const float2 *__restrict__ sc = A.s0_old + c * Mm1;
 
-    // Step 3: E_i[q] = xt[i L - (M-1) + q], xt = {S0, x, zeros}.
+    // E_i[q] = xt[i L - (M-1) + q], xt = {S0, x, zeros}.
     float2 a[G.P];
     const int64_t g0 = i * A.L - Mm1;
     if (active && g0 >= 0 && g0 + G.N <= A.nsamples) {
+        const float2 *__restrict__ xb = xc + g0 + tb;
         static_for<0, G.P>([&](auto Rr) {
             constexpr int r = decltype(Rr)::value;
-            a[r] = xc[g0 + tb + G.TB * pass0_m<LOGN>(r)];
+            a[r] = xb[G.TB * pass0_m<GID>(r)];
         });
     } else {
         static_for<0, G.P>([&](auto Rr) {
             constexpr int r = decltype(Rr)::value;
-            const int64_t g = g0 + tb + G.TB * pass0_m<LOGN>(r);
+            const int64_t g = g0 + tb + G.TB * pass0_m<GID>(r);
             float2 v = make_float2(0.f, 0.f);
             if (active) {
                 if (g < 0)
@@ -100,45 +153,152 @@ __global__ __launch_bounds__(FusedCfg<LOGN>::WG) void ols_fused_kernel(FusedArgs
         });
     }
 
-    // Step 4: F = FFT(E), I = F * H, R = IFFT(I) (1/N is folded into H).
-    forward_all<LOGN>(tb, a, my, A.tw);
-    mul_h<LOGN>(tb, a, A.H);
-    inverse_all<LOGN>(tb, a, my, A.tw);
+    // F = FFT(E), I = F * H, R = IFFT(I) (1/N is folded into H).
+    forward_all<GID>(tb, a, my, tw);
+    mul_h<GID>(a, hp);
+    inverse_all<GID>(tb, a, my, tw);
 
     if (!active) return;
 
-    // Step 5: position q >= M-1 is output i L + q - (M-1).
-    float2 *__restrict__ yc = A.y + c * A.stride;
+    // Position q >= M-1 is output i L + q - (M-1).
+    float2 *__restrict__ yb = A.y + c * A.stride + g0 + tb;
+    const int64_t lim = A.nsamples - g0 - tb;   // q - tb must stay below this
     static_for<0, G.P>([&](auto Rr) {
         constexpr int r = decltype(Rr)::value;
-        const int q = tb + G.TB * pass0_m<LOGN>(r);
-        const int64_t o = g0 + q;
-        if (q >= Mm1 && o < A.nsamples) yc[o] = a[r];
+        constexpr int off = G.TB * pass0_m<GID>(r);
+        if (tb + off >= Mm1 && off < lim) yb[off] = a[r];
     });
 
-    // State carry: the last M-1 samples of {S0, x} of this channel.
-    if (i == A.nblk - 1) {
-        float2 *__restrict__ sn = A.s0_new + c * Mm1;
-        for (int r = tb; r < Mm1; r += G.TB) {
-            const int64_t g = A.nsamples - Mm1 + r;
-            sn[r] = g >= 0 ? xc[g] : sc[Mm1 + g];
+    if (i == A.nblk - 1) carry_state<GID>(A, c, tb, xc, sc);
+}
+
+// The same block for TB >= 64: every wave belongs to one block, so the
+// block's channel, index and buffer descriptors are wave-uniform (SGPRs)
+// and all gathers and stores are buffer accesses with 32-bit offsets.
+template <int GID, class TW, class HP>
+__device__ __forceinline__ void filter_block_wave(const FusedArgs &A, int64_t gb, int tb,
+                                                  float2 *my, const TW &tw, const HP &hp) {
+    constexpr Geo G = make_geo(GID);
+    static_assert(G.TB % 64 == 0, "one block per wave or more");
+    const int64_t total = A.nblk * A.nchan;
+    const bool active = gb < total;
+    const int64_t c = active ? gb / A.nblk : 0;
+    const int64_t i = active ? gb - c * A.nblk : 0;
+    const int Mm1 = A.M - 1;
+    const float2 *__restrict__ xc = A.x + c * A.stride;
+    const float2 *__restrict__ sc = A.s0_old + c * Mm1;
+    const int64_t g0 = i * A.L - Mm1;
+
+    float2 a[G.P];
+    if (active && g0 >= 0 && g0 + G.N <= A.nsamples) {
+        // interior block: one load per point, constant offsets in SGPRs
+        const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc + g0, G.N * 8u);
+        const uint32_t vo = (uint32_t)tb * 8u;
+        static_for<0, G.P>([&](auto Rr) {
+            constexpr int r = decltype(Rr)::value;
+            a[r] = buf_load(rx, vo, (uint32_t)(G.TB * pass0_m<GID>(r) * 8));
+        });
+    } else {
+        // first blocks (state in front) and the partial last block
+        static_for<0, G.P>([&](auto Rr) {
+            constexpr int r = decltype(Rr)::value;
+            const int64_t g = g0 + tb + G.TB * pass0_m<GID>(r);
+            float2 v = make_float2(0.f, 0.f);
+            if (active) {
+                if (g < 0)
+                    v = sc[Mm1 + g];
+                else if (g < A.nsamples)
+                    v = xc[g];
+            }
+            a[r] = v;
+        });
+    }
+
+    forward_all<GID>(tb, a, my, tw);
+    mul_h<GID>(a, hp);
+    inverse_all<GID>(tb, a, my, tw);
+
+    // Outputs i L .. i L + L - 1 come from positions q = M-1 .. N-1; the
+    // descriptor covers the valid outputs only, so the dropped positions
+    // (negative offset) and those past the end fall outside it.
+    int64_t yn = active ? A.nsamples - i * A.L : 0;
+    if (yn > A.L) yn = A.L;
+    if (yn < 0) yn = 0;
+    const __amdgpu_buffer_rsrc_t ry = buf_rsrc(A.y + c * A.stride + i * A.L, (uint32_t)yn * 8u);
+    static_for<0, G.P>([&](auto Rr) {
+        constexpr int r = decltype(Rr)::value;
+        const int q = tb + G.TB * pass0_m<GID>(r);
+        buf_store(a[r], ry, (uint32_t)(q - Mm1) * 8u);
+    });
+
+    if (active && i == A.nblk - 1) carry_state<GID>(A, c, tb, xc, sc);
+}
+
+template <int GID>
+__global__ __launch_bounds__(FusedCfg<GID>::WG) void ols_fused_kernel(FusedArgs A) {
+    using C = FusedCfg<GID>;
+    constexpr Geo G = make_geo(GID);
+    __shared__ float2 lds[C::LDSN];
+
+    const int tid = threadIdx.x;
+    // a block spans whole waves when TB >= 64: make that uniformity visible
+    const int sub = C::WAVE_IO ? __builtin_amdgcn_readfirstlane(tid / G.TB) : tid / G.TB;
+    const int tb = tid - sub * G.TB;
+    float2 *my = lds + sub * G.lds_stride;
+    const int64_t total = A.nblk * A.nchan;
+    const int64_t units = (total + C::BPW - 1) / C::BPW;
+
+    auto run = [&](const auto &tw, const auto &hp) {
+        for (int64_t it = 0;; ++it) {
+            const int64_t unit = unit_of(units, blockIdx.x, gridDim.x, it);
+            if (unit < 0) break;
+            const int64_t gb = unit * C::BPW + sub;
+            if constexpr (C::WAVE_IO)
+                filter_block_wave<GID>(A, gb, tb, my, tw, hp);
+            else
+                filter_block<GID>(A, gb, gb < total, tb, my, tw, hp);
+        }
+    };
+    if constexpr (C::REGS) {
+        TwRegs<GID> tw;
+        tw.load(A.tw, tb);
+        HRegs<GID> hp;
+        hp.load(A.H, tb);
+        run(tw, hp);
+    } else {
+        // Table-fed: re-derive the table pointers every block (an empty asm
+        // hides that they are loop-invariant), so the compiler does not
+        // hoist the table loads out of the loop and spill them.
+        for (int64_t it = 0;; ++it) {
+            const int64_t unit = unit_of(units, blockIdx.x, gridDim.x, it);
+            if (unit < 0) break;
+            const float2 *twp = A.tw;
+            const float2 *hpp = A.H;
+            asm volatile("" : "+s"(twp), "+s"(hpp));
+            const int64_t gb = unit * C::BPW + sub;
+            if constexpr (C::WAVE_IO)
+                filter_block_wave<GID>(A, gb, tb, my, TwTable<GID>{twp, tb},
+                                        HTable<GID>{hpp, tb});
+            else
+                filter_block<GID>(A, gb, gb < total, tb, my, TwTable<GID>{twp, tb},
+                                   HTable<GID>{hpp, tb});
         }
     }
 }
 
 // H[r * TB + tb] = DFT_N(taps)[bin] / N, in the order the fused kernel uses.
-template <int LOGN>
-__global__ __launch_bounds__(make_geo(LOGN).TB) void ols_plan_taps_kernel(
+template <int GID>
+__global__ __launch_bounds__(make_geo(GID).TB) void ols_plan_taps_kernel(
     const float2 *__restrict__ taps, float2 *__restrict__ H, const float2 *__restrict__ tw) {
-    constexpr Geo G = make_geo(LOGN);
+    constexpr Geo G = make_geo(GID);
     __shared__ float2 lds[G.npass > 1 ? G.lds_stride : 1];
     const int tb = threadIdx.x;
     float2 a[G.P];
     static_for<0, G.P>([&](auto Rr) {
         constexpr int r = decltype(Rr)::value;
-        a[r] = taps[tb + G.TB * pass0_m<LOGN>(r)];
+        a[r] = taps[tb + G.TB * pass0_m<GID>(r)];
     });
-    forward_all<LOGN>(tb, a, lds, tw);
+    forward_all<GID>(tb, a, lds, TwTable<GID>{tw, tb});
     constexpr float scale = 1.0f / G.N;
     static_for<0, G.P>([&](auto Rr) {
         constexpr int r = decltype(Rr)::value;
@@ -154,39 +314,74 @@ __global__ __launch_bounds__(256) void copy_kernel(float2 *__restrict__ dst,
         dst[k] = src ? src[k] : make_float2(0.f, 0.f);
 }
 
-template <int LOGN>
-static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t stream) {
-    using C = FusedCfg<LOGN>;
+template <int GID>
+static hipError_t launch_fused_t(const FusedArgs &a, int max_groups, hipStream_t stream) {
+    using C = FusedCfg<GID>;
     const int64_t total = a.nblk * a.nchan;
-    const int64_t grid = (total + C::BPW - 1) / C::BPW;
-    if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(ols_fused_kernel<LOGN>, dim3((unsigned)grid), dim3(C::WG), 0, stream, a);
+    const int64_t units = (total + C::BPW - 1) / C::BPW;
+    if (units <= 0) return hipErrorInvalidConfiguration;
+    int64_t grid = units;
+    if (grid > max_groups) grid = max_groups & ~7;    // persistent, multiple of 8
+    if (grid <= 0) grid = units < max_groups ? units : max_groups;
+    hipLaunchKernelGGL(ols_fused_kernel<GID>, dim3((unsigned)grid), dim3(C::WG), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int LOGN>
+template <int GID>
 static hipError_t launch_plan_t(const float2 *taps, float2 *H, const float2 *tw,
                                 hipStream_t stream) {
-    hipLaunchKernelGGL(ols_plan_taps_kernel<LOGN>, dim3(1), dim3(make_geo(LOGN).TB), 0, stream,
+    hipLaunchKernelGGL(ols_plan_taps_kernel<GID>, dim3(1), dim3(make_geo(GID).TB), 0, stream,
                        taps, H, tw);
     return hipGetLastError();
 }
 
-hipError_t launch_fused(int logn, const FusedArgs &a, hipStream_t stream) {
+hipError_t launch_fused(int logn, const FusedArgs &a, int max_groups, hipStream_t stream) {
     switch (logn) {
-        case 3: return launch_fused_t<3>(a, stream);
-        case 4: return launch_fused_t<4>(a, stream);
-        case 5: return launch_fused_t<5>(a, stream);
-        case 6: return launch_fused_t<6>(a, stream);
-        case 7: return launch_fused_t<7>(a, stream);
-        case 8: return launch_fused_t<8>(a, stream);
-        case 9: return launch_fused_t<9>(a, stream);
-        case 10: return launch_fused_t<10>(a, stream);
-        case 11: return launch_fused_t<11>(a, stream);
-        case 12: return launch_fused_t<12>(a, stream);
-        case 13: return launch_fused_t<13>(a, stream);
-        case 14: return launch_fused_t<14>(a, stream);
+        case 3: return launch_fused_t<3>(a, max_groups, stream);
+        case 4: return launch_fused_t<4>(a, max_groups, stream);
+        case 5: return launch_fused_t<5>(a, max_groups, stream);
+        case 6: return launch_fused_t<6>(a, max_groups, stream);
+        case 7: return launch_fused_t<7>(a, max_groups, stream);
+        case 8: return launch_fused_t<8>(a, max_groups, stream);
+        case 9: return launch_fused_t<9>(a, max_groups, stream);
+        case 10: return launch_fused_t<10>(a, max_groups, stream);
+        case 11: return launch_fused_t<11>(a, max_groups, stream);
+        case 12: return launch_fused_t<12>(a, max_groups, stream);
+        case 13: return launch_fused_t<13>(a, max_groups, stream);
+        case 14: return launch_fused_t<14>(a, max_groups, stream);
         default: return hipErrorInvalidValue;
+    }
+}
+
+template <int GID>
+static int max_groups_t(int cus) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ols_fused_kernel<GID>,
+                                                     FusedCfg<GID>::WG, 0) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    return per_cu * cus;
+}
+
+int fused_max_groups(int logn, int device) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+        cus < 1)
+        cus = 1;
+    switch (logn) {
+        case 3: return max_groups_t<3>(cus);
+        case 4: return max_groups_t<4>(cus);
+        case 5: return max_groups_t<5>(cus);
+        case 6: return max_groups_t<6>(cus);
+        case 7: return max_groups_t<7>(cus);
+        case 8: return max_groups_t<8>(cus);
+        case 9: return max_groups_t<9>(cus);
+        case 10: return max_groups_t<10>(cus);
+        case 11: return max_groups_t<11>(cus);
+        case 12: return max_groups_t<12>(cus);
+        case 13: return max_groups_t<13>(cus);
+        case 14: return max_groups_t<14>(cus);
+        default: return cus;
     }
 }
 

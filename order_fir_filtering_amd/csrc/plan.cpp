@@ -20,6 +20,7 @@ struct fir_ols_plan_s {
     float2 *taps = nullptr;       // N zero-padded taps, staging for set_taps
     float2 *state[2] = {nullptr, nullptr};   // [nchan][M-1] each
     int parity = 0;               // state[parity] is the current state
+    int max_groups = 0;           // resident workgroups of the filtering kernel
     bool has_filter = false;
 };
 
@@ -74,6 +75,8 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
     p->N = N;
     p->L = N - M + 1;
     p->nchan = nchan;
+    p->max_groups = firols::fused_max_groups(logn, p->device);
+    (void)hipGetLastError();
 
     const int ntw = firols::twiddle_count(logn);
     const size_t sbytes = (size_t)state_len(p) * sizeof(float2);
@@ -166,7 +169,7 @@ int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev, int64_t ns
     a.M = (int)p->M;
     a.L = (int)p->L;
     a.nchan = (int)p->nchan;
-    hipError_t e = firols::launch_fused(p->logn, a, (hipStream_t)stream);
+    hipError_t e = firols::launch_fused(p->logn, a, p->max_groups, (hipStream_t)stream);
     if (e != hipSuccess) return FIR_OLS_ERR_HIP;
     if (p->M > 1) p->parity ^= 1;
     return FIR_OLS_OK;
