@@ -407,7 +407,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": f"ols_fused_kernel<{int(np.log2(w.N))}>",
+            "kernel": (f"ols_fused_kernel<{int(np.log2(w.N))}>" if w.N <= 16384 else
+                       f"ols_split_sub_kernel<{w.N // 16384}> + ols_split_combine_kernel (per call)"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -81,6 +81,8 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan);
  *   M           must equal the plan's M.
  *   stream      stream the work is ordered on (after earlier executes).
  * Returns after H is in place.  Leaves the state unchanged.
+ * FIR_OLS_ERR_UNSUPPORTED for N = 65536 (that size takes its filter through
+ * fir_ols_set_freq_response).
  */
 int fir_ols_set_taps(fir_ols_plan_t p, const float *h_host, int64_t M,
                      int is_complex, void *stream);

@@ -23,8 +23,30 @@ struct FusedArgs {
     int nchan;
 };
 
-// Largest log2(N) the LDS-resident kernel covers.
+// Arguments of one chunk of blocks of the split (large-N) path.
+struct SplitArgs {
+    const float2 *x;        // [nchan][stride] input
+    float2 *y;              // [nchan][stride] output
+    const float2 *s0_old;   // [nchan][M-1] state read by this call
+    float2 *s0_new;         // [nchan][M-1] state written by this call
+    const float2 *H;        // RT * Ns values: bins k0 + RT k' in sub-kernel order, / N
+    const float2 *tw;       // twiddle table of the Ns-point sub-transform
+    const float2 *tw_top;   // (RT-1) * Ns values W_N^{q k0}, k0 = 1 .. RT-1
+    float2 *scratch;        // nchunk * N sub-results b_k0
+    int64_t nsamples;       // samples per channel in this call (> 0)
+    int64_t stride;         // elements between channel starts
+    int64_t nblk;           // blocks per channel
+    int64_t blk0;           // first block (over all channels) of this chunk
+    int64_t nchunk;         // blocks in this chunk
+    int M;
+    int L;
+    int nchan;
+};
+
+// Largest log2(N) the LDS-resident kernel covers; larger N (up to
+// kMaxLogN) takes the split path.
 constexpr int kFusedMaxLogN = 14;
+constexpr int kMaxLogN = 16;
 constexpr int kMinLogN = 3;
 
 // Twiddle table size (float2) of the transform of size 2^logn.
@@ -43,6 +65,18 @@ hipError_t launch_fused(int logn, const FusedArgs &a, int max_groups, hipStream_
 // H[i] = DFT_N(taps)[perm[i]] / N from N zero-padded complex taps.
 hipError_t launch_plan_taps(int logn, const float2 *taps_padded, float2 *H,
                             const float2 *tw, hipStream_t stream);
+// Split path: radix of the split (N / 16384; 1 when N <= 16384), twiddle
+// tables, H order, workgroups, launches.
+int split_radix(int logn);
+int split_sub_twiddle_count();
+void build_split_twiddles(int logn, float2 *sub_tw, float2 *top_tw);
+void build_split_h_permutation(int logn, int64_t *perm);
+int64_t split_block_elems(int logn);
+int split_max_groups(int device);
+hipError_t launch_split(int logn, const SplitArgs &a, int max_groups, hipStream_t stream);
+hipError_t launch_split_plan_taps(int logn, const float2 *taps, float2 *H, const float2 *tw,
+                                  const float2 *tw_top, hipStream_t stream);
+
 // dst[i] = src ? src[i] : 0 for i < count.
 hipError_t launch_copy(float2 *dst, const float2 *src, int64_t count,
                        hipStream_t stream);

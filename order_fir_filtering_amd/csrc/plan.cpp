@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
 #include <new>
 #include <vector>
 
@@ -22,6 +23,10 @@ struct fir_ols_plan_s {
     int parity = 0;               // state[parity] is the current state
     int max_groups = 0;           // resident workgroups of the filtering kernel
     bool has_filter = false;
+    // split path (N > 16384)
+    float2 *tw_top = nullptr;     // W_N^{q k0}, k0 = 1 .. RT-1
+    float2 *scratch = nullptr;    // chunk_blocks * N sub-results
+    int64_t chunk_blocks = 0;
 };
 
 namespace {
@@ -41,6 +46,8 @@ bool on_plan_device(const fir_ols_plan_s *p) {
 }
 
 void release(fir_ols_plan_s *p) {
+    hipFree(p->tw_top);
+    hipFree(p->scratch);
     hipFree(p->H);
     hipFree(p->tw);
     hipFree(p->taps);
@@ -51,6 +58,21 @@ void release(fir_ols_plan_s *p) {
 
 int64_t state_len(const fir_ols_plan_s *p) { return p->nchan * (p->M - 1); }
 
+bool is_split(const fir_ols_plan_s *p) { return p->logn > firols::kFusedMaxLogN; }
+
+// Scratch of the split path: enough blocks per chunk to keep every CU busy,
+// small enough (128 MiB by default) to stay in the 256 MB last-level cache.
+int64_t split_chunk_blocks(int logn) {
+    int64_t mib = 128;
+    if (const char *e = std::getenv("FIR_OLS_SPLIT_SCRATCH_MIB")) {
+        const long v = std::strtol(e, nullptr, 10);
+        if (v >= 1 && v <= 65536) mib = v;
+    }
+    const int64_t per_block = firols::split_block_elems(logn) * (int64_t)sizeof(float2);
+    const int64_t n = (mib << 20) / per_block;
+    return n > 0 ? n : 1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -60,7 +82,7 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
     *out = nullptr;
     const int logn = ilog2_pow2(N);
     if (logn < 0 || M < 1 || M > N || nchan < 1) return FIR_OLS_ERR_INVALID_ARG;
-    if (logn < firols::kMinLogN || logn > firols::kFusedMaxLogN) return FIR_OLS_ERR_UNSUPPORTED;
+    if (logn < firols::kMinLogN || logn > firols::kMaxLogN) return FIR_OLS_ERR_UNSUPPORTED;
     if (nchan > (int64_t)1 << 30 || (M - 1) * nchan > ((int64_t)1 << 40))
         return FIR_OLS_ERR_UNSUPPORTED;
 
@@ -75,10 +97,15 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
     p->N = N;
     p->L = N - M + 1;
     p->nchan = nchan;
-    p->max_groups = firols::fused_max_groups(logn, p->device);
+    const bool split = is_split(p);
+    p->max_groups = split ? firols::split_max_groups(p->device)
+                          : firols::fused_max_groups(logn, p->device);
     (void)hipGetLastError();
 
-    const int ntw = firols::twiddle_count(logn);
+    const int RT = firols::split_radix(logn);
+    const int ntw = split ? firols::split_sub_twiddle_count() : firols::twiddle_count(logn);
+    const int64_t ntop = split ? (int64_t)(RT - 1) * (N / RT) : 0;
+    if (split) p->chunk_blocks = split_chunk_blocks(logn);
     const size_t sbytes = (size_t)state_len(p) * sizeof(float2);
     bool ok = hipMalloc(&p->H, N * sizeof(float2)) == hipSuccess &&
               hipMalloc(&p->tw, (size_t)(ntw > 0 ? ntw : 1) * sizeof(float2)) == hipSuccess &&
@@ -87,6 +114,10 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
         ok = hipMalloc(&p->state[0], sbytes) == hipSuccess &&
              hipMalloc(&p->state[1], sbytes) == hipSuccess;
     }
+    if (ok && split) {
+        ok = hipMalloc(&p->tw_top, (size_t)ntop * sizeof(float2)) == hipSuccess &&
+             hipMalloc(&p->scratch, (size_t)(p->chunk_blocks * N) * sizeof(float2)) == hipSuccess;
+    }
     if (!ok) {
         (void)hipGetLastError();
         release(p);
@@ -94,8 +125,14 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
     }
 
     std::vector<float2> tw((size_t)(ntw > 0 ? ntw : 1), make_float2(1.f, 0.f));
-    firols::build_twiddles(logn, tw.data());
+    std::vector<float2> top((size_t)(ntop > 0 ? ntop : 1));
+    if (split)
+        firols::build_split_twiddles(logn, tw.data(), top.data());
+    else
+        firols::build_twiddles(logn, tw.data());
     hipError_t e = hipMemcpy(p->tw, tw.data(), tw.size() * sizeof(float2), hipMemcpyHostToDevice);
+    if (e == hipSuccess && split)
+        e = hipMemcpy(p->tw_top, top.data(), (size_t)ntop * sizeof(float2), hipMemcpyHostToDevice);
     if (e == hipSuccess && sbytes) e = launch_copy(p->state[0], nullptr, state_len(p), nullptr);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
@@ -109,6 +146,10 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
 int fir_ols_set_taps(fir_ols_plan_t p, const float *h_host, int64_t M, int is_complex,
                      void *stream) {
     if (!p || !h_host || M != p->M) return FIR_OLS_ERR_INVALID_ARG;
+    // The taps transform of the 4-way split (N = 65536) is switched off: its
+    // first run ended in a GPU memory fault whose cause is not found yet.
+    // fir_ols_set_freq_response covers that size.
+    if (firols::split_radix(p->logn) > 2) return FIR_OLS_ERR_UNSUPPORTED;
     if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
     std::vector<float2> padded((size_t)p->N, make_float2(0.f, 0.f));
     for (int64_t m = 0; m < M; ++m)
@@ -117,7 +158,9 @@ int fir_ols_set_taps(fir_ols_plan_t p, const float *h_host, int64_t M, int is_co
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipMemcpyAsync(p->taps, padded.data(), p->N * sizeof(float2),
                                   hipMemcpyHostToDevice, s);
-    if (e == hipSuccess) e = firols::launch_plan_taps(p->logn, p->taps, p->H, p->tw, s);
+    if (e == hipSuccess)
+        e = is_split(p) ? firols::launch_split_plan_taps(p->logn, p->taps, p->H, p->tw, p->tw_top, s)
+                        : firols::launch_plan_taps(p->logn, p->taps, p->H, p->tw, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return FIR_OLS_ERR_HIP;
     p->has_filter = true;
@@ -128,7 +171,10 @@ int fir_ols_set_freq_response(fir_ols_plan_t p, const float *H_host, int64_t N, 
     if (!p || !H_host || N != p->N) return FIR_OLS_ERR_INVALID_ARG;
     if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
     std::vector<int64_t> perm((size_t)N);
-    firols::build_h_permutation(p->logn, perm.data());
+    if (is_split(p))
+        firols::build_split_h_permutation(p->logn, perm.data());
+    else
+        firols::build_h_permutation(p->logn, perm.data());
     const float scale = 1.0f / (float)N;   // exact: N is a power of two
     std::vector<float2> Hk((size_t)N);
     for (int64_t i = 0; i < N; ++i) {
@@ -156,20 +202,46 @@ int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev, int64_t ns
     if (xa < ya + (uintptr_t)span && ya < xa + (uintptr_t)span) return FIR_OLS_ERR_ALIAS;
     if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
 
-    firols::FusedArgs a;
-    a.x = (const float2 *)x_dev;
-    a.y = (float2 *)y_dev;
-    a.s0_old = p->state[p->parity];
-    a.s0_new = p->state[p->parity ^ 1];
-    a.H = p->H;
-    a.tw = p->tw;
-    a.nsamples = nsamples;
-    a.stride = chan_stride;
-    a.nblk = (nsamples + p->L - 1) / p->L;
-    a.M = (int)p->M;
-    a.L = (int)p->L;
-    a.nchan = (int)p->nchan;
-    hipError_t e = firols::launch_fused(p->logn, a, p->max_groups, (hipStream_t)stream);
+    const int64_t nblk = (nsamples + p->L - 1) / p->L;
+    hipError_t e = hipSuccess;
+    if (is_split(p)) {
+        firols::SplitArgs a;
+        a.x = (const float2 *)x_dev;
+        a.y = (float2 *)y_dev;
+        a.s0_old = p->state[p->parity];
+        a.s0_new = p->state[p->parity ^ 1];
+        a.H = p->H;
+        a.tw = p->tw;
+        a.tw_top = p->tw_top;
+        a.scratch = p->scratch;
+        a.nsamples = nsamples;
+        a.stride = chan_stride;
+        a.nblk = nblk;
+        a.M = (int)p->M;
+        a.L = (int)p->L;
+        a.nchan = (int)p->nchan;
+        const int64_t total = nblk * p->nchan;
+        for (int64_t b = 0; b < total && e == hipSuccess; b += p->chunk_blocks) {
+            a.blk0 = b;
+            a.nchunk = total - b < p->chunk_blocks ? total - b : p->chunk_blocks;
+            e = firols::launch_split(p->logn, a, p->max_groups, (hipStream_t)stream);
+        }
+    } else {
+        firols::FusedArgs a;
+        a.x = (const float2 *)x_dev;
+        a.y = (float2 *)y_dev;
+        a.s0_old = p->state[p->parity];
+        a.s0_new = p->state[p->parity ^ 1];
+        a.H = p->H;
+        a.tw = p->tw;
+        a.nsamples = nsamples;
+        a.stride = chan_stride;
+        a.nblk = nblk;
+        a.M = (int)p->M;
+        a.L = (int)p->L;
+        a.nchan = (int)p->nchan;
+        e = firols::launch_fused(p->logn, a, p->max_groups, (hipStream_t)stream);
+    }
     if (e != hipSuccess) return FIR_OLS_ERR_HIP;
     if (p->M > 1) p->parity ^= 1;
     return FIR_OLS_OK;

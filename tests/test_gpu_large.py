@@ -1,0 +1,149 @@
+"""GPU parity of the large-N (split) path, N = 32768 and 65536.
+
+Full-size workloads are checked on sampled outputs the float64 oracle
+computes one by one: four whole blocks (first, second, middle, last) plus
+65536 seeded random indices.  Small cases cover every output.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import order_fir_filtering_amd as fo
+import workloads as W
+from gpu_util import check, run_calls, say, to_dev
+
+pytestmark = pytest.mark.gpu
+# The first run of the N = 65536 taps transform (fir_ols_set_taps, 4-way
+# split) faulted the GPU with no cause found on the CPU; that entry point is
+# switched off for N = 65536 and its cases stay skipped until the cause is.
+SKIP_TAPS_65536 = pytest.mark.skip(
+    reason="set_taps at N=65536 is switched off after an unexplained GPU fault")
+THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.set_device(0)
+    fo.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def sampled_indices(w, seed):
+    L, k = w.L, w.samples // w.L
+    blocks = [np.arange(b * L, (b + 1) * L) for b in (0, 1, k // 2, k - 1)]
+    return np.unique(np.concatenate(blocks + [W.sample_indices(seed, w.samples, 65536)]))
+
+
+def test_cfg3_sampled():
+    inp = W.make_inputs("cfg3")
+    w = inp.workload
+    say(f"cfg3: M={w.M} N={w.N} n={w.samples}")
+    with fo.Plan(w.M, w.N) as p:
+        p.set_taps(inp.taps)
+        y = run_calls(p, inp.x, w.calls)
+        st = p.get_state().cpu().numpy()
+    idx = sampled_indices(w, 33)
+    ref = oracle.fir_direct(inp.h_ref, inp.x[0], inp.s0[0], idx=idx, threads=THREADS)
+    check(y[0, idx], ref, inp.h_ref, inp.x, inp.s0, f"cfg3 ({idx.size} outputs)")
+    np.testing.assert_array_equal(st[0], oracle.state_next(inp.x[0], inp.s0[0], w.M))
+
+
+def test_cfg4_frequency_response_sampled():
+    inp = W.make_inputs("cfg4")
+    w = inp.workload
+    say(f"cfg4: M={w.M} N={w.N} n={w.samples} (H given)")
+    with fo.Plan(w.M, w.N) as p:
+        p.set_freq_response(inp.H)
+        y = run_calls(p, inp.x, w.calls)
+    idx = sampled_indices(w, 44)
+    ref = oracle.fir_direct(inp.h_ref, inp.x[0], inp.s0[0], idx=idx, threads=THREADS)
+    check(y[0, idx], ref, inp.h_ref, inp.x, inp.s0, f"cfg4 ({idx.size} outputs)")
+
+
+def _large_cases():
+    rng = np.random.default_rng(77)
+    cases = []
+    for N in (32768, 65536):
+        for M in (1, 2, 1025, N // 3, N):
+            L = N - M + 1
+            for n in sorted({1, max(M - 2, 1), L + 3, 3 * L + int(rng.integers(0, L))}):
+                n = min(n, 300000, 2000 * L)
+                cases.append((N, M, n, int(rng.choice([1, 2])), int(rng.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("N,M,n,nchan,seed", [
+    pytest.param(*c, marks=SKIP_TAPS_65536) if c[0] == 65536 else c for c in _large_cases()])
+def test_large_sizes_small_chunks(N, M, n, nchan, seed, monkeypatch):
+    # a 1 MiB scratch forces a chunk of one or two blocks, so every call
+    # crosses many chunk boundaries
+    monkeypatch.setenv("FIR_OLS_SPLIT_SCRATCH_MIB", "1")
+    say(f"large: N={N} M={M} n={n} nchan={nchan} seed={seed}")
+    rng = np.random.default_rng(seed)
+    h = (rng.standard_normal(M) + 1j * rng.standard_normal(M)).astype(np.complex64)
+    x = W.complex_normal(rng, (nchan, n))
+    s0 = W.complex_normal(rng, (nchan, M - 1))
+    with fo.Plan(M, N, nchan) as p:
+        p.set_taps(h)
+        y = run_calls(p, x, [n], s0=s0)
+        st = p.get_state().cpu().numpy()
+    idx = np.unique(np.concatenate([np.arange(min(n, 3000)), np.arange(max(0, n - 3000), n),
+                                    W.sample_indices(seed, n, 4000)]))
+    ref = oracle.fir_direct_multi(h, x, s0, idx=idx, threads=THREADS)
+    check(y[:, idx], ref, h, x, s0, f"N={N} M={M} n={n}")
+    for c in range(nchan):
+        np.testing.assert_array_equal(st[c], oracle.state_next(x[c], s0[c], M))
+
+
+@pytest.mark.parametrize("N,M", [(32768, 8193), pytest.param(65536, 16385, marks=SKIP_TAPS_65536)])
+def test_large_taps_and_freq_response_agree_and_stream(N, M):
+    say(f"large taps vs H, chunked calls: N={N} M={M}")
+    rng = np.random.default_rng(N + M)
+    h = W.complex_taps(rng, M).astype(np.complex64)
+    L = N - M + 1
+    calls = [L // 2, 1, 2 * L + 5, M - 2, 3 * L]
+    x = W.complex_normal(rng, (1, sum(calls)))
+    with fo.Plan(M, N) as pa, fo.Plan(M, N) as pb:
+        pa.set_taps(h)
+        pb.set_freq_response(W.freq_response_input(h, N))
+        ya = run_calls(pa, x, calls)
+        yb = run_calls(pb, x, [x.shape[1]])
+    idx = np.unique(np.concatenate([np.arange(0, x.shape[1], 7), [x.shape[1] - 1]]))
+    ref = oracle.fir_direct(h, x[0], None, idx=idx, threads=THREADS)
+    check(ya[0, idx], ref, h, x, None, "set_taps, chunked calls")
+    check(yb[0, idx], ref, h, x, None, "set_freq_response")
+
+
+@pytest.mark.parametrize("N,M,d", [(32768, 8193, 8192), (65536, 16385, 12345)])
+def test_large_delay_response(N, M, d):
+    say(f"large delay: N={N} M={M} d={d}")
+    rng = np.random.default_rng(d)
+    x = W.complex_normal(rng, (1, 3 * N))
+    s0 = W.complex_normal(rng, (1, M - 1))
+    H = np.exp(-2j * np.pi * np.arange(N) * d / N).astype(np.complex64)
+    with fo.Plan(M, N) as p:
+        p.set_freq_response(H)
+        y = run_calls(p, x, [x.shape[1]], s0=s0)
+    xt = np.concatenate([s0[0], x[0]])
+    want = xt[M - 1 - d: M - 1 - d + x.shape[1]]
+    check(y, want.astype(np.complex128), np.ones(1), x, s0, "delay")
+
+
+@SKIP_TAPS_65536
+def test_large_repeat_is_bitwise_identical():
+    say("large determinism")
+    rng = np.random.default_rng(3)
+    M, N = 16385, 65536
+    h = rng.standard_normal(M).astype(np.float32)
+    x = W.complex_normal(rng, (1, 400000))
+    outs = []
+    for _ in range(2):
+        with fo.Plan(M, N) as p:
+            p.set_taps(h)
+            outs.append(run_calls(p, x, [123457, 276543]))
+    np.testing.assert_array_equal(outs[0], outs[1])
