@@ -72,12 +72,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uin
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                              0x00020000);
 }
+// Input loads also carry the non-temporal policy: each sample is read by
+// at most two neighbouring blocks close together in time.
 __device__ __forceinline__ float2 buf_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 2));
+}
+// Output stores carry the non-temporal policy (cache-policy bit 1, NT on
+// gfx950): the outputs are not read again, and streaming them out during
+// the kernel leaves fewer dirty L2 lines to write back when it ends.
+constexpr int kStoreNT = 2;
+typedef float nt_float2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void nt_store(float2 *p, float2 v) {
+    __builtin_nontemporal_store(nt_float2{v.x, v.y}, reinterpret_cast<nt_float2 *>(p));
 }
 __device__ __forceinline__ void buf_store(float2 v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(decltype(
-        __builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, voff, 0, 0);
+        __builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, voff, 0, kStoreNT);
 }
 
 // State carry: the last M-1 samples of {S0, x} of channel c go to the new

@@ -92,9 +92,11 @@ __device__ __forceinline__ void filter_block(const FusedArgs &A, int64_t gb, boo
 // The same block for TB >= 64: every wave belongs to one block, so the
 // block's channel, index and buffer descriptors are wave-uniform (SGPRs)
 // and all gathers and stores are buffer accesses with 32-bit offsets.
-template <int GID, class TW, class HP>
-__device__ __forceinline__ void filter_block_wave(const FusedArgs &A, int64_t gb, int tb,
-                                                  float2 *my, const TW &tw, const HP &hp) {
+// Split in two so a kernel can issue a block's input loads before other
+// loads it does not need yet.
+template <int GID>
+__device__ __forceinline__ void gather_block_wave(const FusedArgs &A, int64_t gb, int tb,
+                                                  float2 (&a)[make_geo(GID).P]) {
     constexpr Geo G = make_geo(GID);
     static_assert(G.TB % 64 == 0, "one block per wave or more");
     const int64_t total = A.nblk * A.nchan;
@@ -105,8 +107,6 @@ __device__ __forceinline__ void filter_block_wave(const FusedArgs &A, int64_t gb
     const float2 *__restrict__ xc = A.x + c * A.stride;
     const float2 *__restrict__ sc = A.s0_old + c * Mm1;
     const int64_t g0 = i * A.L - Mm1;
-
-    float2 a[G.P];
     if (active && g0 >= 0 && g0 + G.N <= A.nsamples) {
         // interior block: one load per point, constant offsets in SGPRs
         const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc + g0, G.N * 8u);
@@ -130,6 +130,18 @@ __device__ __forceinline__ void filter_block_wave(const FusedArgs &A, int64_t gb
             a[r] = v;
         });
     }
+}
+
+template <int GID, class TW, class HP>
+__device__ __forceinline__ void process_block_wave(const FusedArgs &A, int64_t gb, int tb,
+                                                   float2 (&a)[make_geo(GID).P], float2 *my,
+                                                   const TW &tw, const HP &hp) {
+    constexpr Geo G = make_geo(GID);
+    const int64_t total = A.nblk * A.nchan;
+    const bool active = gb < total;
+    const int64_t c = active ? gb / A.nblk : 0;
+    const int64_t i = active ? gb - c * A.nblk : 0;
+    const int Mm1 = A.M - 1;
 
     forward_all<GID>(tb, a, my, tw);
     mul_h<GID>(a, hp);
@@ -148,7 +160,9 @@ __device__ __forceinline__ void filter_block_wave(const FusedArgs &A, int64_t gb
         buf_store(a[r], ry, (uint32_t)(q - Mm1) * 8u);
     });
 
-    if (active && i == A.nblk - 1) carry_state<GID>(A.nsamples, Mm1, tb, xc, sc, A.s0_new + c * Mm1);
+    if (active && i == A.nblk - 1)
+        carry_state<GID>(A.nsamples, Mm1, tb, A.x + c * A.stride, A.s0_old + c * Mm1,
+                         A.s0_new + c * Mm1);
 }
 
 template <int GID>
@@ -170,13 +184,38 @@ __global__ __launch_bounds__(FusedCfg<GID>::WG) void ols_fused_kernel(FusedArgs 
             const int64_t unit = unit_of(units, blockIdx.x, gridDim.x, it);
             if (unit < 0) break;
             const int64_t gb = unit * C::BPW + sub;
-            if constexpr (C::WAVE_IO)
-                filter_block_wave<GID>(A, gb, tb, my, tw, hp);
-            else
-                filter_block<GID>(A, gb, gb < total, tb, my, tw, hp);
+            filter_block<GID>(A, gb, gb < total, tb, my, tw, hp);
         }
     };
-    if constexpr (C::REGS) {
+    if constexpr (C::WAVE_IO && C::REGS) {
+        // the first block's input is requested before the register-held
+        // twiddles and H, so the first pass only waits for its own data;
+        // later blocks' inputs are requested right after the stores
+        float2 a[G.P];
+        int64_t unit = unit_of(units, blockIdx.x, gridDim.x, 0);
+        if (unit >= 0) gather_block_wave<GID>(A, unit * C::BPW + sub, tb, a);
+        TwRegs<GID> tw;
+        tw.load(A.tw, tb);
+        HRegs<GID> hp;
+        hp.load(A.H, tb);
+        for (int64_t it = 1; unit >= 0; ++it) {
+            process_block_wave<GID>(A, unit * C::BPW + sub, tb, a, my, tw, hp);
+            unit = unit_of(units, blockIdx.x, gridDim.x, it);
+            if (unit >= 0) gather_block_wave<GID>(A, unit * C::BPW + sub, tb, a);
+        }
+    } else if constexpr (C::WAVE_IO) {
+        for (int64_t it = 0;; ++it) {
+            const int64_t unit = unit_of(units, blockIdx.x, gridDim.x, it);
+            if (unit < 0) break;
+            const float2 *twp = A.tw;
+            const float2 *hpp = A.H;
+            asm volatile("" : "+s"(twp), "+s"(hpp));
+            const int64_t gb = unit * C::BPW + sub;
+            float2 a[G.P];
+            gather_block_wave<GID>(A, gb, tb, a);
+            process_block_wave<GID>(A, gb, tb, a, my, TwTable<GID>{twp, tb}, HTable<GID>{hpp, tb});
+        }
+    } else if constexpr (C::REGS) {
         TwRegs<GID> tw;
         tw.load(A.tw, tb);
         HRegs<GID> hp;
@@ -193,12 +232,8 @@ __global__ __launch_bounds__(FusedCfg<GID>::WG) void ols_fused_kernel(FusedArgs 
             const float2 *hpp = A.H;
             asm volatile("" : "+s"(twp), "+s"(hpp));
             const int64_t gb = unit * C::BPW + sub;
-            if constexpr (C::WAVE_IO)
-                filter_block_wave<GID>(A, gb, tb, my, TwTable<GID>{twp, tb},
-                                        HTable<GID>{hpp, tb});
-            else
-                filter_block<GID>(A, gb, gb < total, tb, my, TwTable<GID>{twp, tb},
-                                   HTable<GID>{hpp, tb});
+            filter_block<GID>(A, gb, gb < total, tb, my, TwTable<GID>{twp, tb},
+                              HTable<GID>{hpp, tb});
         }
     }
 }

@@ -146,7 +146,7 @@ __device__ __forceinline__ void split_sub_loop(const SplitArgs &A, const SplitOr
             const int q = tb + kSub.TB * pass0_m<kSubGid>(r);
             float2 v = a[r];
             if constexpr (K0 > 0) v = cmulc(v, ttp[(K0 - 1) * kSub.N + q]);
-            out[q] = v;
+            nt_store(out + q, v);   // read once by the combine kernel
         });
 
         if (K0 == 0 && i == A.nblk - 1)
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256) void ols_split_combine_kernel(SplitArgs A) {
             });
             const int n = q + j * kSub.N;
             const int64_t o = o0 + n;
-            if (n >= Mm1 && o < A.nsamples) yc[o] = s;
+            if (n >= Mm1 && o < A.nsamples) nt_store(yc + o, s);
         });
     }
 }
