@@ -1,4 +1,4 @@
-// Register-resident small DFTs (radix 2, 4, 8, 16) and complex helpers.
+// Register-resident small DFTs (radix 2, 4, 8, 16, 32) and complex helpers.
 //
 // dft<R, DIR> replaces a[0..R) by X[k] = sum_j a[j] * exp(DIR * 2 pi i j k / R),
 // natural order in and out; DIR = -1 is the forward transform, +1 the
@@ -6,7 +6,7 @@
 // index j = R2*j1 + j2 and output index k = k1 + R1*k2:
 //   X[k1 + R1 k2] = sum_j2 W_R^{j2 k1} (sum_j1 a[R2 j1 + j2] W_R1^{j1 k1}) W_R2^{j2 k2}.
 // Every index is a compile-time constant, so the arrays live in VGPRs and
-// all constant rotations (multiples of pi/8) fold into adds and at most
+// all constant rotations (multiples of pi/16) fold into adds and at most
 // four multiplies.
 #pragma once
 
@@ -74,6 +74,30 @@ __host__ __device__ __forceinline__ float2 rot16(float2 a) {
     }
 }
 
+// a * exp(i * A * pi / 16) for a compile-time A: even A reduce to rot16;
+// odd A use cos/sin of the odd multiples of pi/16 (values of the first
+// octant, mapped by symmetry).
+template <int A>
+__host__ __device__ __forceinline__ float2 rot32(float2 a) {
+    constexpr int e = ((A % 32) + 32) % 32;
+    if constexpr (e % 2 == 0) {
+        return rot16<e / 2>(a);
+    } else {
+        constexpr float c1 = 0.980785280403230449f;  // cos(pi/16)
+        constexpr float s1 = 0.195090322016128268f;  // sin(pi/16)
+        constexpr float c3 = 0.831469612302545237f;  // cos(3pi/16)
+        constexpr float s3 = 0.555570233019602225f;  // sin(3pi/16)
+        // (cos, sin) of e*pi/16 for odd e from the quadrant and the octant
+        constexpr int q = e / 8;           // quadrant: e*pi/16 in [q*pi/2, (q+1)*pi/2)
+        constexpr int r = e % 8;           // 1, 3, 5, 7
+        constexpr float cr = r == 1 ? c1 : r == 3 ? c3 : r == 5 ? s3 : s1;
+        constexpr float sr = r == 1 ? s1 : r == 3 ? s3 : r == 5 ? c3 : c1;
+        constexpr float c = q == 0 ? cr : q == 1 ? -sr : q == 2 ? -cr : sr;
+        constexpr float s = q == 0 ? sr : q == 1 ? cr : q == 2 ? -sr : -cr;
+        return make_float2(fmaf(a.x, c, -a.y * s), fmaf(a.x, s, a.y * c));
+    }
+}
+
 template <int R, int DIR>
 __host__ __device__ __forceinline__ void dft(float2 (&a)[R]);
 
@@ -107,7 +131,7 @@ __host__ __device__ __forceinline__ void dft_split(float2 (&a)[R1 * R2]) {
         dft<R1, DIR>(t);
         static_for<0, R1>([&](auto K1) {
             constexpr int k1 = decltype(K1)::value;
-            y[R2 * k1 + j2] = rot16<DIR * j2 * k1 * (16 / R)>(t[k1]);
+            y[R2 * k1 + j2] = rot32<DIR * j2 * k1 * (32 / R)>(t[k1]);
         });
     });
     static_for<0, R1>([&](auto K1) {
@@ -121,7 +145,7 @@ __host__ __device__ __forceinline__ void dft_split(float2 (&a)[R1 * R2]) {
 
 template <int R, int DIR>
 __host__ __device__ __forceinline__ void dft(float2 (&a)[R]) {
-    static_assert(R == 1 || R == 2 || R == 4 || R == 8 || R == 16, "radix");
+    static_assert(R == 1 || R == 2 || R == 4 || R == 8 || R == 16 || R == 32, "radix");
     if constexpr (R == 2) {
         dft2<DIR>(a);
     } else if constexpr (R == 4) {
@@ -130,6 +154,8 @@ __host__ __device__ __forceinline__ void dft(float2 (&a)[R]) {
         dft_split<2, 4, DIR>(a);
     } else if constexpr (R == 16) {
         dft_split<4, 4, DIR>(a);
+    } else if constexpr (R == 32) {
+        dft_split<4, 8, DIR>(a);
     }
 }
 

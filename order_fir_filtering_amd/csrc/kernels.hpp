@@ -49,12 +49,14 @@ constexpr int kFusedMaxLogN = 14;
 constexpr int kMaxLogN = 16;
 constexpr int kMinLogN = 3;
 
-// Twiddle table size (float2) of the transform of size 2^logn.
-int twiddle_count(int logn);
+// The table builders take a geometry id (geo_id(logn, logp)); a plain
+// log2(N) selects the default geometry of that size.
+// Twiddle table size (float2) of the transform of geometry gid.
+int twiddle_count(int gid);
 // Fill the twiddle table (host memory), computed in double, rounded to float.
-void build_twiddles(int logn, float2 *host_out);
+void build_twiddles(int gid, float2 *host_out);
 // perm[i]: the spectrum bin whose value the kernels expect at H[i].
-void build_h_permutation(int logn, int64_t *perm);
+void build_h_permutation(int gid, int64_t *perm);
 
 // Workgroups of the filtering kernel that fit on the device at once
 // (resident workgroups per CU times CUs); the kernel is persistent and

@@ -364,10 +364,10 @@ hipError_t launch_copy(float2 *dst, const float2 *src, int64_t count, hipStream_
     return hipGetLastError();
 }
 
-int twiddle_count(int logn) { return make_geo(logn).twoff[make_geo(logn).npass]; }
+int twiddle_count(int gid) { return make_geo(gid).twoff[make_geo(gid).npass]; }
 
-void build_twiddles(int logn, float2 *out) {
-    const Geo g = make_geo(logn);
+void build_twiddles(int gid, float2 *out) {
+    const Geo g = make_geo(gid);
     for (int s = 0; s < g.npass; ++s) {
         const int R = g.R[s], S = g.S[s];
         const int64_t span = (int64_t)S * R;
@@ -382,8 +382,8 @@ void build_twiddles(int logn, float2 *out) {
     }
 }
 
-void build_h_permutation(int logn, int64_t *perm) {
-    const Geo g = make_geo(logn);
+void build_h_permutation(int gid, int64_t *perm) {
+    const Geo g = make_geo(gid);
     for (int r = 0; r < g.P; ++r)
         for (int tb = 0; tb < g.TB; ++tb)
             perm[(int64_t)r * g.TB + tb] = bin_of_position(g, last_pass_position(g, tb, r));

@@ -27,8 +27,14 @@ namespace firols {
 
 namespace {
 
-constexpr int kSubGid = 14;                 // Ns = 16384, P = 16, 1024 threads
+// Ns = 16384 points per workgroup: 512 threads x 32 points, radices 16, 32,
+// 32 (two LDS exchanges per direction).  Pass 0's twiddles stay in 15
+// registers per thread for the whole kernel (the second virtual thread's
+// follow by a constant rotation); pass 1's table (992 values) is copied to
+// LDS once.  No twiddle comes from global memory inside the loop.
+constexpr int kSubGid = geo_id(14, 5);
 constexpr Geo kSub = make_geo(kSubGid);
+constexpr int kGroup = 16;                  // loads in flight per group
 
 // v * W_RT^{e} with W_RT = exp(DIR * 2 pi i / RT), RT in {2, 4}, e constant.
 template <int RT, int DIR, int E>
@@ -37,32 +43,75 @@ __device__ __forceinline__ float2 wrt(float2 v) {
     return rot16<DIR * e * (16 / RT)>(v);
 }
 
-// a_k0 of the sub-problem K0 for the registers of thread tb, one input
-// quarter (or half) at a time: the scheduling barriers keep at most P loads
-// in flight, which the 128-VGPR budget of a 1024-thread workgroup needs.
-template <int RT, int K0, class LOAD>
-__device__ __forceinline__ void split_gather(float2 (&a)[kSub.P], int tb, const LOAD &load,
+// a_k0 of sub-problem k0 for the registers of thread tb:
+//   RT = 2:  a = e0 + s e1,
+//   RT = 4:  a = (e0 + s e2) + (-i)^k0 (e1 + s e3),   s = (-1)^k0,
+// (the k0-th output of a radix-RT DFT over e_j = E[q + j Ns]), then times
+// W_N^{q k0}.  k0 is a runtime value uniform over the workgroup, so one code
+// path serves every k0.  Points go kGather at a time, with scheduling
+// barriers, so at most RT * kGather loads are in flight.
+constexpr int kGather = 8;
+template <int RT, class LOAD>
+__device__ __forceinline__ void split_gather(float2 (&a)[kSub.P], int tb, int k0,
+                                             const LOAD &load,
                                              const float2 *__restrict__ tw_top) {
-    static_for<0, kSub.P>([&](auto Rr) {
-        constexpr int r = decltype(Rr)::value;
-        a[r] = load(tb + kSub.TB * pass0_m<kSubGid>(r));
-    });
-    static_for<1, RT>([&](auto J) {
-        constexpr int j = decltype(J)::value;
+    static_assert(RT == 2 || RT == 4, "split radix");
+    const float sg = (k0 & 1) ? -1.f : 1.f;
+    // (-i)^k0 = (ca, sa): k0 = 0: (1, 0), 1: (0, -1), 2: (-1, 0), 3: (0, 1)
+    const float ca = (k0 & 1) ? 0.f : ((k0 & 2) ? -1.f : 1.f);
+    const float sa = (k0 & 1) ? ((k0 & 2) ? 1.f : -1.f) : 0.f;
+    static_for<0, kSub.P / kGather>([&](auto Gx) {
+        constexpr int g = decltype(Gx)::value;
         __builtin_amdgcn_sched_barrier(0);
-        static_for<0, kSub.P>([&](auto Rr) {
-            constexpr int r = decltype(Rr)::value;
-            const float2 e = load(tb + kSub.TB * pass0_m<kSubGid>(r) + j * kSub.N);
-            a[r] = cadd(a[r], wrt<RT, -1, j * K0>(e));
+        float2 e[RT][kGather];
+        static_for<0, kGather>([&](auto Rr) {
+            constexpr int r = g * kGather + decltype(Rr)::value;
+            const int q = tb + kSub.TB * pass0_m<kSubGid>(r);
+            static_for<0, RT>([&](auto J) {
+                e[decltype(J)::value][decltype(Rr)::value] = load(q + decltype(J)::value * kSub.N);
+            });
+        });
+        static_for<0, kGather>([&](auto Rr) {
+            constexpr int r = g * kGather + decltype(Rr)::value;
+            constexpr int i = decltype(Rr)::value;
+            if constexpr (RT == 2) {
+                a[r] = make_float2(fmaf(sg, e[1][i].x, e[0][i].x), fmaf(sg, e[1][i].y, e[0][i].y));
+            } else {
+                const float2 u = make_float2(fmaf(sg, e[2][i].x, e[0][i].x),
+                                             fmaf(sg, e[2][i].y, e[0][i].y));
+                const float2 v = make_float2(fmaf(sg, e[3][i].x, e[1][i].x),
+                                             fmaf(sg, e[3][i].y, e[1][i].y));
+                a[r] = make_float2(fmaf(ca, v.x, fmaf(-sa, v.y, u.x)),
+                                   fmaf(ca, v.y, fmaf(sa, v.x, u.y)));
+            }
         });
     });
-    if constexpr (K0 > 0) {
-        __builtin_amdgcn_sched_barrier(0);
-        static_for<0, kSub.P>([&](auto Rr) {
-            constexpr int r = decltype(Rr)::value;
-            a[r] = cmul(a[r], tw_top[(K0 - 1) * kSub.N + tb + kSub.TB * pass0_m<kSubGid>(r)]);
+    if (k0 > 0) {
+        const float2 *__restrict__ tt = tw_top + (int64_t)(k0 - 1) * kSub.N + tb;
+        static_for<0, kSub.P / kGather>([&](auto Gx) {
+            constexpr int g = decltype(Gx)::value;
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, kGather>([&](auto Rr) {
+                constexpr int r = g * kGather + decltype(Rr)::value;
+                a[r] = cmul(a[r], tt[kSub.TB * pass0_m<kSubGid>(r)]);
+            });
         });
     }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Product with the bins k0 + RT k' of H (sub-kernel order), in groups.
+__device__ __forceinline__ void split_mul_h(float2 (&a)[kSub.P], int tb,
+                                            const float2 *__restrict__ H) {
+    static_for<0, kSub.P / kGroup>([&](auto Gx) {
+        constexpr int g = decltype(Gx)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, kGroup>([&](auto Rr) {
+            constexpr int r = g * kGroup + decltype(Rr)::value;
+            a[r] = cmul(a[r], H[r * kSub.TB + tb]);
+        });
+    });
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Work order of the sub-kernel: workgroup w always runs sub-problem k0 of
@@ -96,13 +145,14 @@ __device__ __forceinline__ SplitOrder split_order(int w, int G, int64_t nblocks)
     return o;
 }
 
-// The persistent loop of a workgroup with sub-problem K0.
-template <int RT, int K0>
+// The persistent loop of a workgroup (sub-problem o.k0 of its team's blocks).
+template <int RT>
 __device__ __forceinline__ void split_sub_loop(const SplitArgs &A, const SplitOrder &o,
-                                               float2 *lds) {
+                                               float2 *lds, const TwRegLds<kSubGid> &tw) {
     constexpr int N = kSub.N * RT;
     const int tb = threadIdx.x;
     const int Mm1 = A.M - 1;
+    const int k0 = o.k0;
     for (int64_t lb = o.first; lb < o.end; lb += o.step) {
         const int64_t gb = A.blk0 + lb;
         const int64_t c = gb / A.nblk;
@@ -111,13 +161,13 @@ __device__ __forceinline__ void split_sub_loop(const SplitArgs &A, const SplitOr
         const float2 *__restrict__ sc = A.s0_old + c * Mm1;
         const int64_t g0 = i * A.L - Mm1;
         // table pointers re-derived per block so their loads stay in the loop
-        const float2 *twp = A.tw, *hp = A.H, *ttp = A.tw_top;
-        asm volatile("" : "+s"(twp), "+s"(hp), "+s"(ttp));
+        const float2 *hp = A.H, *ttp = A.tw_top;
+        asm volatile("" : "+s"(hp), "+s"(ttp));
 
         float2 a[kSub.P];
         if (g0 >= 0 && g0 + N <= A.nsamples) {
             const float2 *__restrict__ xb = xc + g0;
-            split_gather<RT, K0>(a, tb, [&](int q) { return xb[q]; }, ttp);
+            split_gather<RT>(a, tb, k0, [&](int q) { return xb[q]; }, ttp);
         } else {
             // first blocks (state in front) and the partial last block: two
             // range-checked loads per point, one over the valid input and one
@@ -129,27 +179,32 @@ __device__ __forceinline__ void split_sub_loop(const SplitArgs &A, const SplitOr
             const __amdgpu_buffer_rsrc_t rs = buf_rsrc(sc, g0 < 0 ? (uint32_t)Mm1 * 8u : 0u);
             const int dx = (int)(g0 - xs);          // <= 0
             const int ds = (int)(g0 + Mm1);         // >= 0
-            split_gather<RT, K0>(a, tb, [&](int q) {
+            split_gather<RT>(a, tb, k0, [&](int q) {
                 const float2 u = buf_load(rx, (uint32_t)(q + dx) * 8u, 0);
                 const float2 v = buf_load(rs, (uint32_t)(q + ds) * 8u, 0);
                 return make_float2(u.x + v.x, u.y + v.y);
             }, ttp);
         }
 
-        forward_all<kSubGid>(tb, a, lds, TwTable<kSubGid>{twp, tb});
-        mul_h<kSubGid>(a, HTable<kSubGid>{hp + K0 * kSub.N, tb});
-        inverse_all<kSubGid>(tb, a, lds, TwTable<kSubGid>{twp, tb});
+        forward_all<kSubGid>(tb, a, lds, tw);
+        split_mul_h(a, tb, hp + (int64_t)k0 * kSub.N);
+        inverse_all<kSubGid>(tb, a, lds, tw);
 
-        float2 *__restrict__ out = A.scratch + lb * N + K0 * kSub.N;
-        static_for<0, kSub.P>([&](auto Rr) {
-            constexpr int r = decltype(Rr)::value;
-            const int q = tb + kSub.TB * pass0_m<kSubGid>(r);
-            float2 v = a[r];
-            if constexpr (K0 > 0) v = cmulc(v, ttp[(K0 - 1) * kSub.N + q]);
-            nt_store(out + q, v);   // read once by the combine kernel
+        float2 *__restrict__ out = A.scratch + lb * N + (int64_t)k0 * kSub.N;
+        const float2 *__restrict__ tt = ttp + (int64_t)(k0 > 0 ? k0 - 1 : 0) * kSub.N;
+        static_for<0, kSub.P / kGroup>([&](auto Gx) {
+            constexpr int g = decltype(Gx)::value;
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, kGroup>([&](auto Rr) {
+                constexpr int r = g * kGroup + decltype(Rr)::value;
+                const int q = tb + kSub.TB * pass0_m<kSubGid>(r);
+                float2 v = a[r];
+                if (k0 > 0) v = cmulc(v, tt[q]);
+                nt_store(out + q, v);   // read once by the combine kernel
+            });
         });
 
-        if (K0 == 0 && i == A.nblk - 1)
+        if (k0 == 0 && i == A.nblk - 1)
             carry_state<kSubGid>(A.nsamples, Mm1, tb, xc, sc, A.s0_new + c * Mm1);
     }
 }
@@ -158,14 +213,16 @@ __device__ __forceinline__ void split_sub_loop(const SplitArgs &A, const SplitOr
 
 template <int RT>
 __global__ __launch_bounds__(kSub.TB) void ols_split_sub_kernel(SplitArgs A) {
-    __shared__ float2 lds[kSub.lds_stride];
+    // exchange buffer, then the pass-1 twiddle table
+    __shared__ float2 lds[kSub.lds_stride + TwRegLds<kSubGid>::lds_count];
     const SplitOrder o = split_order<RT>(blockIdx.x, gridDim.x, A.nchunk);
-    switch (o.k0) {
-        case 0: split_sub_loop<RT, 0>(A, o, lds); break;
-        case 1: split_sub_loop<RT, 1>(A, o, lds); break;
-        case 2: if constexpr (RT > 2) split_sub_loop<RT, 2>(A, o, lds); break;
-        default: if constexpr (RT > 3) split_sub_loop<RT, 3>(A, o, lds); break;
-    }
+    float2 *lds_tw = lds + kSub.lds_stride;
+    for (int e = threadIdx.x; e < TwRegLds<kSubGid>::lds_count; e += kSub.TB)
+        lds_tw[e] = A.tw[kSub.twoff[1] + e];
+    __syncthreads();
+    TwRegLds<kSubGid> tw;
+    tw.load(A.tw, lds_tw, threadIdx.x);
+    split_sub_loop<RT>(A, o, lds, tw);
 }
 
 // One thread per (block, q): y[q + j Ns] = sum_k0 W_RT^{-j k0} b_k0[q].
@@ -210,13 +267,7 @@ __global__ __launch_bounds__(kSub.TB) void ols_split_plan_taps_kernel(
     const int tb = threadIdx.x;
     const int k0 = blockIdx.x;
     float2 a[kSub.P];
-    auto load = [&](int q) { return taps[q]; };
-    switch (k0) {
-        case 0: split_gather<RT, 0>(a, tb, load, tw_top); break;
-        case 1: split_gather<RT, 1>(a, tb, load, tw_top); break;
-        case 2: if constexpr (RT > 2) split_gather<RT, 2>(a, tb, load, tw_top); break;
-        default: if constexpr (RT > 3) split_gather<RT, 3>(a, tb, load, tw_top); break;
-    }
+    split_gather<RT>(a, tb, k0, [&](int q) { return taps[q]; }, tw_top);
     forward_all<kSubGid>(tb, a, lds, TwTable<kSubGid>{tw, tb});
     constexpr float scale = 1.0f / (kSub.N * RT);
     static_for<0, kSub.P>([&](auto Rr) {
@@ -225,7 +276,7 @@ __global__ __launch_bounds__(kSub.TB) void ols_split_plan_taps_kernel(
     });
 }
 
-int split_radix(int logn) { return logn > kFusedMaxLogN ? 1 << (logn - kSubGid) : 1; }
+int split_radix(int logn) { return logn > kFusedMaxLogN ? 1 << (logn - kSub.logn) : 1; }
 
 int split_sub_twiddle_count() { return twiddle_count(kSubGid); }
 
