@@ -4,7 +4,8 @@
 // complex points in registers (P = 16 by default, or N itself when N < 16).  The
 // transform is an in-place mixed-radix decimation-in-frequency FFT with
 // radices R[0..npass-1] (one smaller radix pass first when log2(N) is not a
-// multiple of log2(P), then radix-P passes).  Pass s works at stride
+// multiple of log2(R), then radix-R passes; R = P unless the geometry id
+// asks for a smaller R).  Pass s works at stride
 // S[s] = N / (R[0] * ... * R[s]):
 //
 //   virtual thread v in [0, N/R[s]),  K = v / S[s],  t = v % S[s]
@@ -32,24 +33,30 @@ struct Geo {
     int lds_stride;            // padded LDS slots of one block (float2)
 };
 
-// A geometry id packs log2(N) (low byte) and, optionally, log2(P) (next
-// byte; 0 selects the default P = 16, or N when N < 16).
-constexpr int geo_id(int logn, int logp = 0) { return logn | (logp << 8); }
+// A geometry id packs log2(N) (low byte), optionally log2(P) (next byte;
+// 0 selects the default P = 16, or N when N < 16) and optionally log2 of
+// the pass radix (third byte; 0 selects radix P).  With a radix below P a
+// thread runs P / radix virtual threads in every pass.
+constexpr int geo_id(int logn, int logp = 0, int logr = 0) {
+    return logn | (logp << 8) | (logr << 16);
+}
 
 constexpr Geo make_geo(int gid) {
     Geo g{};
     const int logn = gid & 0xff;
-    int logp = gid >> 8;
+    int logp = (gid >> 8) & 0xff;
     if (logp == 0) logp = logn >= 4 ? 4 : logn;
+    int logr = (gid >> 16) & 0xff;
+    if (logr == 0 || logr > logp) logr = logp;
     g.logn = logn;
     g.logp = logp;
     g.N = 1 << logn;
     g.P = 1 << logp;
     g.TB = g.N / g.P;
     int np = 0;
-    const int rem = logn % logp;
+    const int rem = logn % logr;
     if (rem) g.R[np++] = 1 << rem;
-    for (int i = 0; i < logn / logp; ++i) g.R[np++] = g.P;
+    for (int i = 0; i < logn / logr; ++i) g.R[np++] = 1 << logr;
     g.npass = np;
     int S = g.N;
     g.twoff[0] = 0;

@@ -43,9 +43,10 @@ struct SplitArgs {
     int nchan;
 };
 
-// Largest log2(N) the LDS-resident kernel covers; larger N (up to
-// kMaxLogN) takes the split path.
+// Largest log2(N) the LDS-resident kernel covers; N = 2^kBigLogN takes the
+// half-resident kernel, larger N (up to kMaxLogN) the split path.
 constexpr int kFusedMaxLogN = 14;
+constexpr int kBigLogN = 15;
 constexpr int kMaxLogN = 16;
 constexpr int kMinLogN = 3;
 
@@ -67,7 +68,14 @@ hipError_t launch_fused(int logn, const FusedArgs &a, int max_groups, hipStream_
 // H[i] = DFT_N(taps)[perm[i]] / N from N zero-padded complex taps.
 hipError_t launch_plan_taps(int logn, const float2 *taps_padded, float2 *H,
                             const float2 *tw, hipStream_t stream);
-// Split path: radix of the split (N / 16384; 1 when N <= 16384), twiddle
+// Half-resident kernel for N = 2^kBigLogN: its geometry id (for the
+// table builders), resident workgroups, launches.
+int big_geometry();
+int big_max_groups(int device);
+hipError_t launch_big(const FusedArgs &a, int max_groups, hipStream_t stream);
+hipError_t launch_big_plan_taps(const float2 *taps_padded, float2 *H, const float2 *tw,
+                                hipStream_t stream);
+// Split path: radix of the split (N / 16384; 1 when N <= 2^kBigLogN), twiddle
 // tables, H order, workgroups, launches.
 int split_radix(int logn);
 int split_sub_twiddle_count();

@@ -7,6 +7,7 @@
 
 #include <cstdint>
 
+#include "kernels.hpp"
 #include "ols_phases.hpp"
 
 namespace firols {
@@ -77,6 +78,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uin
 __device__ __forceinline__ float2 buf_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 2));
 }
+// Loads of the plan's tables (twiddles, H), which every block reads again:
+// default cache policy.
+__device__ __forceinline__ float2 buf_load_cached(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                  uint32_t soff) {
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
 // Output stores carry the non-temporal policy (cache-policy bit 1, NT on
 // gfx950): the outputs are not read again, and streaming them out during
 // the kernel leaves fewer dirty L2 lines to write back when it ends.
@@ -102,6 +109,99 @@ __device__ __forceinline__ void carry_state(int64_t nsamples, int Mm1, int tb,
         const int64_t g = nsamples - Mm1 + r;
         sn[r] = g >= 0 ? xc[g] : sc[Mm1 + g];
     }
+}
+
+// The same block for TB >= 64: every wave belongs to one block, so the
+// block's channel, index and buffer descriptors are wave-uniform (SGPRs)
+// and all gathers and stores are buffer accesses with 32-bit offsets.
+// Split in two so a kernel can issue a block's input loads before other
+// loads it does not need yet.  With BUF_EDGE the first and last blocks
+// also gather through buffer descriptors (two range-checked loads per
+// point: one over the valid input, one over the state), which keeps the
+// per-point address registers of large P out of the kernel.
+template <int GID, bool BUF_EDGE = false>
+__device__ __forceinline__ void gather_block_wave(const FusedArgs &A, int64_t gb, int tb,
+                                                  float2 (&a)[make_geo(GID).P]) {
+    constexpr Geo G = make_geo(GID);
+    static_assert(G.TB % 64 == 0, "one block per wave or more");
+    const int64_t total = A.nblk * A.nchan;
+    const bool active = gb < total;
+    const int64_t c = active ? gb / A.nblk : 0;
+    const int64_t i = active ? gb - c * A.nblk : 0;
+    const int Mm1 = A.M - 1;
+    const float2 *__restrict__ xc = A.x + c * A.stride;
+    const float2 *__restrict__ sc = A.s0_old + c * Mm1;
+    const int64_t g0 = i * A.L - Mm1;
+    if (active && g0 >= 0 && g0 + G.N <= A.nsamples) {
+        // interior block: one load per point, constant offsets in SGPRs
+        const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc + g0, G.N * 8u);
+        const uint32_t vo = (uint32_t)tb * 8u;
+        static_for<0, G.P>([&](auto Rr) {
+            constexpr int r = decltype(Rr)::value;
+            a[r] = buf_load(rx, vo, (uint32_t)(G.TB * pass0_m<GID>(r) * 8));
+        });
+    } else if constexpr (BUF_EDGE) {
+        // first blocks (state in front) and the partial last block: the
+        // whole offset sits in the range-checked VGPR operand; at most one
+        // of the two loads is in range, the other reads zero
+        const int64_t xs = active && g0 > 0 ? g0 : 0;
+        int64_t xn = active ? A.nsamples - xs : 0;
+        xn = xn < 0 ? 0 : (xn > G.N ? G.N : xn);
+        const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc + xs, (uint32_t)xn * 8u);
+        const __amdgpu_buffer_rsrc_t rs =
+            buf_rsrc(sc, active && g0 < 0 ? (uint32_t)Mm1 * 8u : 0u);
+        const int dx = (int)(g0 - xs) + tb;     // q + dx indexes x from xs
+        const int ds = (int)(g0 + Mm1) + tb;    // q + ds indexes the state
+        static_for<0, G.P>([&](auto Rr) {
+            constexpr int off = G.TB * pass0_m<GID>(decltype(Rr)::value);
+            const float2 u = buf_load(rx, (uint32_t)(off + dx) * 8u, 0);
+            const float2 v = buf_load(rs, (uint32_t)(off + ds) * 8u, 0);
+            a[decltype(Rr)::value] = make_float2(u.x + v.x, u.y + v.y);
+        });
+    } else {
+        // first blocks (state in front) and the partial last block
+        static_for<0, G.P>([&](auto Rr) {
+            constexpr int r = decltype(Rr)::value;
+            const int64_t g = g0 + tb + G.TB * pass0_m<GID>(r);
+            float2 v = make_float2(0.f, 0.f);
+            if (active) {
+                if (g < 0)
+                    v = sc[Mm1 + g];
+                else if (g < A.nsamples)
+                    v = xc[g];
+            }
+            a[r] = v;
+        });
+    }
+}
+
+// Store of a block's kept points (step 5) from the pass-0 layout, and the
+// state carry of the channel's last block.  Outputs i L .. i L + L - 1
+// come from positions q = M-1 .. N-1; the descriptor covers the valid
+// outputs only, so the dropped positions (negative offset) and those past
+// the end fall outside it.
+template <int GID>
+__device__ __forceinline__ void store_block_wave(const FusedArgs &A, int64_t gb, int tb,
+                                                 const float2 (&a)[make_geo(GID).P]) {
+    constexpr Geo G = make_geo(GID);
+    const int64_t total = A.nblk * A.nchan;
+    const bool active = gb < total;
+    const int64_t c = active ? gb / A.nblk : 0;
+    const int64_t i = active ? gb - c * A.nblk : 0;
+    const int Mm1 = A.M - 1;
+    int64_t yn = active ? A.nsamples - i * A.L : 0;
+    if (yn > A.L) yn = A.L;
+    if (yn < 0) yn = 0;
+    const __amdgpu_buffer_rsrc_t ry = buf_rsrc(A.y + c * A.stride + i * A.L, (uint32_t)yn * 8u);
+    static_for<0, G.P>([&](auto Rr) {
+        constexpr int r = decltype(Rr)::value;
+        const int q = tb + G.TB * pass0_m<GID>(r);
+        buf_store(a[r], ry, (uint32_t)(q - Mm1) * 8u);
+    });
+
+    if (active && i == A.nblk - 1)
+        carry_state<GID>(A.nsamples, Mm1, tb, A.x + c * A.stride, A.s0_old + c * Mm1,
+                         A.s0_new + c * Mm1);
 }
 
 }  // namespace firols

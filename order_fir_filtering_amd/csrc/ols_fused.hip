@@ -89,80 +89,15 @@ __device__ __forceinline__ void filter_block(const FusedArgs &A, int64_t gb, boo
     if (i == A.nblk - 1) carry_state<GID>(A.nsamples, Mm1, tb, xc, sc, A.s0_new + c * Mm1);
 }
 
-// The same block for TB >= 64: every wave belongs to one block, so the
-// block's channel, index and buffer descriptors are wave-uniform (SGPRs)
-// and all gathers and stores are buffer accesses with 32-bit offsets.
-// Split in two so a kernel can issue a block's input loads before other
-// loads it does not need yet.
-template <int GID>
-__device__ __forceinline__ void gather_block_wave(const FusedArgs &A, int64_t gb, int tb,
-                                                  float2 (&a)[make_geo(GID).P]) {
-    constexpr Geo G = make_geo(GID);
-    static_assert(G.TB % 64 == 0, "one block per wave or more");
-    const int64_t total = A.nblk * A.nchan;
-    const bool active = gb < total;
-    const int64_t c = active ? gb / A.nblk : 0;
-    const int64_t i = active ? gb - c * A.nblk : 0;
-    const int Mm1 = A.M - 1;
-    const float2 *__restrict__ xc = A.x + c * A.stride;
-    const float2 *__restrict__ sc = A.s0_old + c * Mm1;
-    const int64_t g0 = i * A.L - Mm1;
-    if (active && g0 >= 0 && g0 + G.N <= A.nsamples) {
-        // interior block: one load per point, constant offsets in SGPRs
-        const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc + g0, G.N * 8u);
-        const uint32_t vo = (uint32_t)tb * 8u;
-        static_for<0, G.P>([&](auto Rr) {
-            constexpr int r = decltype(Rr)::value;
-            a[r] = buf_load(rx, vo, (uint32_t)(G.TB * pass0_m<GID>(r) * 8));
-        });
-    } else {
-        // first blocks (state in front) and the partial last block
-        static_for<0, G.P>([&](auto Rr) {
-            constexpr int r = decltype(Rr)::value;
-            const int64_t g = g0 + tb + G.TB * pass0_m<GID>(r);
-            float2 v = make_float2(0.f, 0.f);
-            if (active) {
-                if (g < 0)
-                    v = sc[Mm1 + g];
-                else if (g < A.nsamples)
-                    v = xc[g];
-            }
-            a[r] = v;
-        });
-    }
-}
-
 template <int GID, class TW, class HP>
 __device__ __forceinline__ void process_block_wave(const FusedArgs &A, int64_t gb, int tb,
                                                    float2 (&a)[make_geo(GID).P], float2 *my,
                                                    const TW &tw, const HP &hp) {
-    constexpr Geo G = make_geo(GID);
-    const int64_t total = A.nblk * A.nchan;
-    const bool active = gb < total;
-    const int64_t c = active ? gb / A.nblk : 0;
-    const int64_t i = active ? gb - c * A.nblk : 0;
-    const int Mm1 = A.M - 1;
-
     forward_all<GID>(tb, a, my, tw);
     mul_h<GID>(a, hp);
     inverse_all<GID>(tb, a, my, tw);
 
-    // Outputs i L .. i L + L - 1 come from positions q = M-1 .. N-1; the
-    // descriptor covers the valid outputs only, so the dropped positions
-    // (negative offset) and those past the end fall outside it.
-    int64_t yn = active ? A.nsamples - i * A.L : 0;
-    if (yn > A.L) yn = A.L;
-    if (yn < 0) yn = 0;
-    const __amdgpu_buffer_rsrc_t ry = buf_rsrc(A.y + c * A.stride + i * A.L, (uint32_t)yn * 8u);
-    static_for<0, G.P>([&](auto Rr) {
-        constexpr int r = decltype(Rr)::value;
-        const int q = tb + G.TB * pass0_m<GID>(r);
-        buf_store(a[r], ry, (uint32_t)(q - Mm1) * 8u);
-    });
-
-    if (active && i == A.nblk - 1)
-        carry_state<GID>(A.nsamples, Mm1, tb, A.x + c * A.stride, A.s0_old + c * Mm1,
-                         A.s0_new + c * Mm1);
+    store_block_wave<GID>(A, gb, tb, a);
 }
 
 template <int GID>

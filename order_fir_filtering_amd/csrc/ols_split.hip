@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kSub.TB) void ols_split_plan_taps_kernel(
     });
 }
 
-int split_radix(int logn) { return logn > kFusedMaxLogN ? 1 << (logn - kSub.logn) : 1; }
+int split_radix(int logn) { return logn > kBigLogN ? 1 << (logn - kSub.logn) : 1; }
 
 int split_sub_twiddle_count() { return twiddle_count(kSubGid); }
 

@@ -58,7 +58,12 @@ void release(fir_ols_plan_s *p) {
 
 int64_t state_len(const fir_ols_plan_s *p) { return p->nchan * (p->M - 1); }
 
-bool is_split(const fir_ols_plan_s *p) { return p->logn > firols::kFusedMaxLogN; }
+bool is_split(const fir_ols_plan_s *p) { return p->logn > firols::kBigLogN; }
+bool is_big(const fir_ols_plan_s *p) { return p->logn == firols::kBigLogN; }
+// geometry id of the plan's table builders (fused and half-resident paths)
+int table_geometry(const fir_ols_plan_s *p) {
+    return is_big(p) ? firols::big_geometry() : p->logn;
+}
 
 // Scratch of the split path: enough blocks per chunk to keep every CU busy,
 // small enough (128 MiB by default) to stay in the 256 MB last-level cache.
@@ -98,12 +103,13 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
     p->L = N - M + 1;
     p->nchan = nchan;
     const bool split = is_split(p);
-    p->max_groups = split ? firols::split_max_groups(p->device)
-                          : firols::fused_max_groups(logn, p->device);
+    p->max_groups = split       ? firols::split_max_groups(p->device)
+                    : is_big(p) ? firols::big_max_groups(p->device)
+                                : firols::fused_max_groups(logn, p->device);
     (void)hipGetLastError();
 
     const int RT = firols::split_radix(logn);
-    const int ntw = split ? firols::split_sub_twiddle_count() : firols::twiddle_count(logn);
+    const int ntw = split ? firols::split_sub_twiddle_count() : firols::twiddle_count(table_geometry(p));
     const int64_t ntop = split ? (int64_t)(RT - 1) * (N / RT) : 0;
     if (split) p->chunk_blocks = split_chunk_blocks(logn);
     const size_t sbytes = (size_t)state_len(p) * sizeof(float2);
@@ -129,7 +135,7 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
     if (split)
         firols::build_split_twiddles(logn, tw.data(), top.data());
     else
-        firols::build_twiddles(logn, tw.data());
+        firols::build_twiddles(table_geometry(p), tw.data());
     hipError_t e = hipMemcpy(p->tw, tw.data(), tw.size() * sizeof(float2), hipMemcpyHostToDevice);
     if (e == hipSuccess && split)
         e = hipMemcpy(p->tw_top, top.data(), (size_t)ntop * sizeof(float2), hipMemcpyHostToDevice);
@@ -160,6 +166,7 @@ int fir_ols_set_taps(fir_ols_plan_t p, const float *h_host, int64_t M, int is_co
                                   hipMemcpyHostToDevice, s);
     if (e == hipSuccess)
         e = is_split(p) ? firols::launch_split_plan_taps(p->logn, p->taps, p->H, p->tw, p->tw_top, s)
+            : is_big(p) ? firols::launch_big_plan_taps(p->taps, p->H, p->tw, s)
                         : firols::launch_plan_taps(p->logn, p->taps, p->H, p->tw, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return FIR_OLS_ERR_HIP;
@@ -174,7 +181,7 @@ int fir_ols_set_freq_response(fir_ols_plan_t p, const float *H_host, int64_t N, 
     if (is_split(p))
         firols::build_split_h_permutation(p->logn, perm.data());
     else
-        firols::build_h_permutation(p->logn, perm.data());
+        firols::build_h_permutation(table_geometry(p), perm.data());
     const float scale = 1.0f / (float)N;   // exact: N is a power of two
     std::vector<float2> Hk((size_t)N);
     for (int64_t i = 0; i < N; ++i) {
@@ -240,7 +247,8 @@ int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev, int64_t ns
         a.M = (int)p->M;
         a.L = (int)p->L;
         a.nchan = (int)p->nchan;
-        e = firols::launch_fused(p->logn, a, p->max_groups, (hipStream_t)stream);
+        e = is_big(p) ? firols::launch_big(a, p->max_groups, (hipStream_t)stream)
+                      : firols::launch_fused(p->logn, a, p->max_groups, (hipStream_t)stream);
     }
     if (e != hipSuccess) return FIR_OLS_ERR_HIP;
     if (p->M > 1) p->parity ^= 1;
