@@ -127,17 +127,25 @@ __device__ __forceinline__ void pass0_twiddles(float2 (&a)[64], const TW &tw) {
     });
     __builtin_amdgcn_sched_barrier(0);
 }
-template <int U, class TW>
-__device__ __forceinline__ void fwd_pass0_first(float2 (&a)[64], const TW &tw) {
+// Forward pass 0 of virtual thread U with its twiddles of k < 16 already
+// in registers (requested before the previous block's stores: memory
+// operations complete in order, stores included, so a load issued after a
+// burst of stores would wait for the burst).
+template <int U>
+__device__ __forceinline__ void fwd_pass0_first(float2 (&a)[64], const float2 (&w)[15]) {
     __builtin_amdgcn_sched_barrier(0);
-    float2 w[15];
-    static_for<1, 16>([&](auto Kk) { w[decltype(Kk)::value - 1] = tw(ic<0>{}, ic<U>{}, Kk); });
     dft_at<32, -1, 32 * U>(a);
     static_for<1, 16>([&](auto Kk) {
         constexpr int k = decltype(Kk)::value;
         a[32 * U + k] = cmul(a[32 * U + k], w[k - 1]);
     });
     __builtin_amdgcn_sched_barrier(0);
+}
+template <int U, int K0, int N, class TW>
+__device__ __forceinline__ void load_pass0_twiddles(float2 (&w)[N], const TW &tw) {
+    static_for<0, N>([&](auto Ii) {
+        w[decltype(Ii)::value] = tw(ic<0>{}, ic<U>{}, ic<K0 + decltype(Ii)::value>{});
+    });
 }
 
 // Passes 1 and 2 (forward), the product with H and inverse passes 2 and 1
@@ -149,12 +157,21 @@ __device__ __forceinline__ void big_half(int tb, float2 *lds, const TW &tw,
     get_run<33>(lds + slot1(tb), c);
     fwd_vt<1, H>(c, tw);
     put_run<33>(lds + slot1(tb), c);
+    // this half's H is requested before the barrier, so its latency
+    // overlaps the wait and the pass-2 DFT
+    __builtin_amdgcn_sched_barrier(0);
+    float2 hv[32];
+    static_for<0, 32>([&](auto Kk) {
+        constexpr int k = decltype(Kk)::value;
+        hv[k] = buf_load_cached(Hp, (uint32_t)tb * 8u, (uint32_t)(32 * H + k) * kBig.TB * 8u);
+    });
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     get_run<1>(lds + slot2(tb), c);
     fwd_vt<2, H>(c, tw);
     static_for<0, 32>([&](auto Kk) {
         constexpr int k = decltype(Kk)::value;
-        c[k] = cmul(c[k], buf_load_cached(Hp, (uint32_t)tb * 8u, (uint32_t)(32 * H + k) * kBig.TB * 8u));
+        c[k] = cmul(c[k], hv[k]);
     });
     inv_vt<2, H>(c, tw);
     put_run<1>(lds + slot2(tb), c);
@@ -166,17 +183,23 @@ __device__ __forceinline__ void big_half(int tb, float2 *lds, const TW &tw,
 }
 
 // Step 4 of one block, ending in the store: a holds the gathered block in
-// the pass-0 layout; out(ic<U>, a) stores virtual thread U's 32 results
-// (registers 32 U .. 32 U + 31 of a, pass-0 layout) once they are final.
-template <class TW, class OUT>
-__device__ __forceinline__ void big_transform(int tb, float2 (&a)[64], float2 *lds, const TW &tw,
-                                              __amdgpu_buffer_rsrc_t Hp, const OUT &out) {
+// the pass-0 layout and w0, w1 the forward pass-0 twiddles of k < 16 of
+// both virtual threads; out(ic<U>, a) stores virtual thread U's 32 results
+// (registers 32 U .. 32 U + 31 of a, pass-0 layout) once they are final,
+// and next(ic<U>, a) may then refill those registers (the next block's
+// input, requested while this block finishes).  w0, w1 are reloaded for
+// the next block before the last stores.
+template <class TW, class OUT, class NEXT>
+__device__ __forceinline__ void big_transform(int tb, float2 (&a)[64], float2 (&w0)[15],
+                                              float2 (&w1)[15], float2 *lds, const TW &tw,
+                                              __amdgpu_buffer_rsrc_t Hp, const OUT &out,
+                                              const NEXT &next) {
     // forward pass 0; the first half's outputs go to LDS as soon as a
     // virtual thread is done
-    fwd_pass0_first<0>(a, tw);
+    fwd_pass0_first<0>(a, w0);
     __syncthreads();                 // the previous block's readers of LDS are done
     put0<0, 0>(tb, a, lds);
-    fwd_pass0_first<1>(a, tw);
+    fwd_pass0_first<1>(a, w1);
     put0<1, 0>(tb, a, lds);
     __syncthreads();
     big_half<0>(tb, lds, tw, Hp);
@@ -196,11 +219,26 @@ __device__ __forceinline__ void big_transform(int tb, float2 (&a)[64], float2 *l
     get0<0, 1>(tb, a, lds);
     pass0_twiddles<0, 16, 32, true>(a, tw);
     dft_at<32, 1, 0>(a);
+    // virtual thread 1's twiddles come before the stores and the next
+    // block's input
+    __builtin_amdgcn_sched_barrier(0);
+    float2 wi[16];
+    load_pass0_twiddles<1, 16>(wi, tw);
+    __builtin_amdgcn_sched_barrier(0);
     out(ic<0>{}, a);
+    next(ic<0>{}, a);
     get0<1, 1>(tb, a, lds);
-    pass0_twiddles<1, 16, 32, true>(a, tw);
+    static_for<16, 32>([&](auto Kk) {
+        constexpr int k = decltype(Kk)::value;
+        a[32 + k] = cmulc(a[32 + k], wi[k - 16]);
+    });
     dft_at<32, 1, 32>(a);
+    __builtin_amdgcn_sched_barrier(0);
+    load_pass0_twiddles<0, 1>(w0, tw);
+    load_pass0_twiddles<1, 1>(w1, tw);
+    __builtin_amdgcn_sched_barrier(0);
     out(ic<1>{}, a);
+    next(ic<1>{}, a);
 }
 
 }  // namespace
@@ -212,14 +250,21 @@ __global__ __launch_bounds__(kBig.TB) void ols_big_kernel(FusedArgs A) {
     for (int e = tb; e < kTw1; e += kBig.TB) lds_tw[e] = A.tw[kBig.twoff[1] + e];
     // (the first barrier of the transform orders these writes before use)
     const int64_t units = A.nblk * A.nchan;
-    for (int64_t it = 0;; ++it) {
-        const int64_t gb = unit_of(units, blockIdx.x, gridDim.x, it);
-        if (gb < 0) break;
+    // software-pipelined over blocks: the input of the next block is
+    // requested as soon as the registers of a virtual thread are free
+    int64_t gb = unit_of(units, blockIdx.x, gridDim.x, 0);
+    float2 a[kBig.P], w0[15], w1[15];
+    if (gb >= 0) {
+        gather_block_wave<kBigGid, true>(A, gb, tb, a);
+        const TwBig tw0{buf_rsrc(A.tw, (uint32_t)kBig.twoff[kBig.npass] * 8u), lds_tw, tb};
+        load_pass0_twiddles<0, 1>(w0, tw0);
+        load_pass0_twiddles<1, 1>(w1, tw0);
+    }
+    for (int64_t it = 1; gb >= 0; ++it) {
+        const int64_t gn = unit_of(units, blockIdx.x, gridDim.x, it);
         // table pointers re-derived per block so their loads stay in the loop
         const float2 *twp = A.tw, *hp = A.H;
         asm volatile("" : "+s"(twp), "+s"(hp));
-        float2 a[kBig.P];
-        gather_block_wave<kBigGid, true>(A, gb, tb, a);
         // step 5: outputs i L .. i L + L - 1 are positions M-1 .. N-1; the
         // descriptor covers the valid outputs only, so the dropped
         // positions (negative offsets) and those past the end fall outside
@@ -233,16 +278,23 @@ __global__ __launch_bounds__(kBig.TB) void ols_big_kernel(FusedArgs A) {
         const int qo = tb - Mm1;
         const __amdgpu_buffer_rsrc_t rtw = buf_rsrc(twp, (uint32_t)kBig.twoff[kBig.npass] * 8u);
         const __amdgpu_buffer_rsrc_t rh = buf_rsrc(hp, (uint32_t)kBig.N * 8u);
-        big_transform(tb, a, lds, TwBig{rtw, lds_tw, tb}, rh, [&](auto Uu, const float2(&v)[64]) {
-            constexpr int u = decltype(Uu)::value;
-            static_for<0, 32>([&](auto J) {
-                constexpr int r = 32 * u + decltype(J)::value;
-                buf_store(v[r], ry, (uint32_t)(qo + kBig.TB * pass0_m<kBigGid>(r)) * 8u);
+        big_transform(
+            tb, a, w0, w1, lds, TwBig{rtw, lds_tw, tb}, rh,
+            [&](auto Uu, const float2(&v)[64]) {
+                constexpr int u = decltype(Uu)::value;
+                static_for<0, 32>([&](auto J) {
+                    constexpr int r = 32 * u + decltype(J)::value;
+                    buf_store(v[r], ry, (uint32_t)(qo + kBig.TB * pass0_m<kBigGid>(r)) * 8u);
+                });
+            },
+            [&](auto Uu, float2(&v)[64]) {
+                constexpr int u = decltype(Uu)::value;
+                if (gn >= 0) gather_block_wave<kBigGid, true, 32 * u, 32 * u + 32>(A, gn, tb, v);
             });
-        });
         if (i == A.nblk - 1)
             carry_state<kBigGid>(A.nsamples, Mm1, tb, A.x + c * A.stride, A.s0_old + c * Mm1,
                                  A.s0_new + c * Mm1);
+        gb = gn;
     }
 }
 
@@ -258,9 +310,12 @@ __global__ __launch_bounds__(kBig.TB) void ols_big_plan_taps_kernel(
         constexpr int r = decltype(Rr)::value;
         a[r] = taps[tb + kBig.TB * pass0_m<kBigGid>(r)];
     });
-    fwd_pass0_first<0>(a, twt);
+    float2 w[15];
+    load_pass0_twiddles<0, 1>(w, twt);
+    fwd_pass0_first<0>(a, w);
     put0<0, 0>(tb, a, lds);
-    fwd_pass0_first<1>(a, twt);
+    load_pass0_twiddles<1, 1>(w, twt);
+    fwd_pass0_first<1>(a, w);
     put0<1, 0>(tb, a, lds);
     constexpr float scale = 1.0f / kBig.N;
     static_for<0, 2>([&](auto Hh) {

@@ -119,7 +119,8 @@ __device__ __forceinline__ void carry_state(int64_t nsamples, int Mm1, int tb,
 // also gather through buffer descriptors (two range-checked loads per
 // point: one over the valid input, one over the state), which keeps the
 // per-point address registers of large P out of the kernel.
-template <int GID, bool BUF_EDGE = false>
+// R0 .. R1 selects the registers to fill (default: all).
+template <int GID, bool BUF_EDGE = false, int R0 = 0, int R1 = make_geo(GID).P>
 __device__ __forceinline__ void gather_block_wave(const FusedArgs &A, int64_t gb, int tb,
                                                   float2 (&a)[make_geo(GID).P]) {
     constexpr Geo G = make_geo(GID);
@@ -136,7 +137,7 @@ __device__ __forceinline__ void gather_block_wave(const FusedArgs &A, int64_t gb
         // interior block: one load per point, constant offsets in SGPRs
         const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc + g0, G.N * 8u);
         const uint32_t vo = (uint32_t)tb * 8u;
-        static_for<0, G.P>([&](auto Rr) {
+        static_for<R0, R1>([&](auto Rr) {
             constexpr int r = decltype(Rr)::value;
             a[r] = buf_load(rx, vo, (uint32_t)(G.TB * pass0_m<GID>(r) * 8));
         });
@@ -152,7 +153,7 @@ __device__ __forceinline__ void gather_block_wave(const FusedArgs &A, int64_t gb
             buf_rsrc(sc, active && g0 < 0 ? (uint32_t)Mm1 * 8u : 0u);
         const int dx = (int)(g0 - xs) + tb;     // q + dx indexes x from xs
         const int ds = (int)(g0 + Mm1) + tb;    // q + ds indexes the state
-        static_for<0, G.P>([&](auto Rr) {
+        static_for<R0, R1>([&](auto Rr) {
             constexpr int off = G.TB * pass0_m<GID>(decltype(Rr)::value);
             const float2 u = buf_load(rx, (uint32_t)(off + dx) * 8u, 0);
             const float2 v = buf_load(rs, (uint32_t)(off + ds) * 8u, 0);
@@ -160,7 +161,7 @@ __device__ __forceinline__ void gather_block_wave(const FusedArgs &A, int64_t gb
         });
     } else {
         // first blocks (state in front) and the partial last block
-        static_for<0, G.P>([&](auto Rr) {
+        static_for<R0, R1>([&](auto Rr) {
             constexpr int r = decltype(Rr)::value;
             const int64_t g = g0 + tb + G.TB * pass0_m<GID>(r);
             float2 v = make_float2(0.f, 0.f);
