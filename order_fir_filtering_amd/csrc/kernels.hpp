@@ -31,8 +31,8 @@ struct SplitArgs {
     float2 *s0_new;         // [nchan][M-1] state written by this call
     const float2 *H;        // RT * Ns values: bins k0 + RT k' in sub-kernel order, / N
     const float2 *tw;       // twiddle table of the Ns-point sub-transform
-    const float2 *tw_top;   // (RT-1) * Ns values W_N^{q k0}, k0 = 1 .. RT-1
-    float2 *scratch;        // nchunk * N sub-results b_k0
+    const float2 *tw_top;   // RT * Ns values W_N^{q k0}, k0 = 0 .. RT-1 (row 0 all ones)
+    float2 *scratch;        // nchunk * N sub-results c_k0
     int64_t nsamples;       // samples per channel in this call (> 0)
     int64_t stride;         // elements between channel starts
     int64_t nblk;           // blocks per channel
@@ -75,17 +75,16 @@ int big_max_groups(int device);
 hipError_t launch_big(const FusedArgs &a, int max_groups, hipStream_t stream);
 hipError_t launch_big_plan_taps(const float2 *taps_padded, float2 *H, const float2 *tw,
                                 hipStream_t stream);
-// Split path: radix of the split (N / 16384; 1 when N <= 2^kBigLogN), twiddle
-// tables, H order, workgroups, launches.
+// Split path (N = 65536): radix of the split (N / 32768; 1 when
+// N <= 2^kBigLogN), twiddle tables, H order, workgroups, launches.
 int split_radix(int logn);
 int split_sub_twiddle_count();
+int64_t split_top_twiddle_count(int logn);
 void build_split_twiddles(int logn, float2 *sub_tw, float2 *top_tw);
 void build_split_h_permutation(int logn, int64_t *perm);
 int64_t split_block_elems(int logn);
 int split_max_groups(int device);
 hipError_t launch_split(int logn, const SplitArgs &a, int max_groups, hipStream_t stream);
-hipError_t launch_split_plan_taps(int logn, const float2 *taps, float2 *H, const float2 *tw,
-                                  const float2 *tw_top, hipStream_t stream);
 
 // dst[i] = src ? src[i] : 0 for i < count.
 hipError_t launch_copy(float2 *dst, const float2 *src, int64_t count,

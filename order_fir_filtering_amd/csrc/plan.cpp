@@ -24,7 +24,7 @@ struct fir_ols_plan_s {
     int max_groups = 0;           // resident workgroups of the filtering kernel
     bool has_filter = false;
     // split path (N > 16384)
-    float2 *tw_top = nullptr;     // W_N^{q k0}, k0 = 1 .. RT-1
+    float2 *tw_top = nullptr;     // W_N^{q k0}, k0 = 0 .. RT-1
     float2 *scratch = nullptr;    // chunk_blocks * N sub-results
     int64_t chunk_blocks = 0;
 };
@@ -108,9 +108,8 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
                                 : firols::fused_max_groups(logn, p->device);
     (void)hipGetLastError();
 
-    const int RT = firols::split_radix(logn);
     const int ntw = split ? firols::split_sub_twiddle_count() : firols::twiddle_count(table_geometry(p));
-    const int64_t ntop = split ? (int64_t)(RT - 1) * (N / RT) : 0;
+    const int64_t ntop = split ? firols::split_top_twiddle_count(logn) : 0;
     if (split) p->chunk_blocks = split_chunk_blocks(logn);
     const size_t sbytes = (size_t)state_len(p) * sizeof(float2);
     bool ok = hipMalloc(&p->H, N * sizeof(float2)) == hipSuccess &&
@@ -152,10 +151,10 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
 int fir_ols_set_taps(fir_ols_plan_t p, const float *h_host, int64_t M, int is_complex,
                      void *stream) {
     if (!p || !h_host || M != p->M) return FIR_OLS_ERR_INVALID_ARG;
-    // The taps transform of the 4-way split (N = 65536) is switched off: its
-    // first run ended in a GPU memory fault whose cause is not found yet.
-    // fir_ols_set_freq_response covers that size.
-    if (firols::split_radix(p->logn) > 2) return FIR_OLS_ERR_UNSUPPORTED;
+    // The taps transform of the split path (N = 65536) is switched off: an
+    // earlier version of it ended in a GPU memory fault whose cause is not
+    // found yet.  fir_ols_set_freq_response covers that size.
+    if (is_split(p)) return FIR_OLS_ERR_UNSUPPORTED;
     if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
     std::vector<float2> padded((size_t)p->N, make_float2(0.f, 0.f));
     for (int64_t m = 0; m < M; ++m)
@@ -165,9 +164,8 @@ int fir_ols_set_taps(fir_ols_plan_t p, const float *h_host, int64_t M, int is_co
     hipError_t e = hipMemcpyAsync(p->taps, padded.data(), p->N * sizeof(float2),
                                   hipMemcpyHostToDevice, s);
     if (e == hipSuccess)
-        e = is_split(p) ? firols::launch_split_plan_taps(p->logn, p->taps, p->H, p->tw, p->tw_top, s)
-            : is_big(p) ? firols::launch_big_plan_taps(p->taps, p->H, p->tw, s)
-                        : firols::launch_plan_taps(p->logn, p->taps, p->H, p->tw, s);
+        e = is_big(p) ? firols::launch_big_plan_taps(p->taps, p->H, p->tw, s)
+                      : firols::launch_plan_taps(p->logn, p->taps, p->H, p->tw, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return FIR_OLS_ERR_HIP;
     p->has_filter = true;
