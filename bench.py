@@ -408,7 +408,7 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": (f"ols_fused_kernel<{int(np.log2(w.N))}>" if w.N <= 16384 else
-                       f"ols_split_sub_kernel<{w.N // 16384}> + ols_split_combine_kernel (per call)"),
+                       "ols_big_kernel" if w.N == 32768 else "ols_split_kernel"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -23,7 +23,7 @@ struct FusedArgs {
     int nchan;
 };
 
-// Arguments of one chunk of blocks of the split (large-N) path.
+// Arguments of one call of the split (N = 65536) path.
 struct SplitArgs {
     const float2 *x;        // [nchan][stride] input
     float2 *y;              // [nchan][stride] output
@@ -32,12 +32,10 @@ struct SplitArgs {
     const float2 *H;        // RT * Ns values: bins k0 + RT k' in sub-kernel order, / N
     const float2 *tw;       // twiddle table of the Ns-point sub-transform
     const float2 *tw_top;   // RT * Ns values W_N^{q k0}, k0 = 0 .. RT-1 (row 0 all ones)
-    float2 *scratch;        // nchunk * N sub-results c_k0
+    float2 *scratch;        // one slot of RT * Ns values per resident workgroup
     int64_t nsamples;       // samples per channel in this call (> 0)
     int64_t stride;         // elements between channel starts
     int64_t nblk;           // blocks per channel
-    int64_t blk0;           // first block (over all channels) of this chunk
-    int64_t nchunk;         // blocks in this chunk
     int M;
     int L;
     int nchan;
@@ -82,7 +80,7 @@ int split_sub_twiddle_count();
 int64_t split_top_twiddle_count(int logn);
 void build_split_twiddles(int logn, float2 *sub_tw, float2 *top_tw);
 void build_split_h_permutation(int logn, int64_t *perm);
-int64_t split_block_elems(int logn);
+int64_t split_slot_elems(int logn);
 int split_max_groups(int device);
 hipError_t launch_split(int logn, const SplitArgs &a, int max_groups, hipStream_t stream);
 

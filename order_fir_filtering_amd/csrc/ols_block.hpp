@@ -96,6 +96,13 @@ __device__ __forceinline__ void buf_store(float2 v, __amdgpu_buffer_rsrc_t r, ui
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(decltype(
         __builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, voff, 0, kStoreNT);
 }
+// Default-policy store with a scalar offset, for scratch data that is read
+// back soon (all in range).
+__device__ __forceinline__ void buf_store_cached(float2 v, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(decltype(
+        __builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, voff, soff, 0);
+}
 // The same with a scalar offset, for stores that are all in range (the
 // range check is not relied on, so the constant part may sit in soff).
 __device__ __forceinline__ void buf_store_so(float2 v, __amdgpu_buffer_rsrc_t r, uint32_t voff,

@@ -6,7 +6,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <cstdlib>
 #include <new>
 #include <vector>
 
@@ -25,8 +24,7 @@ struct fir_ols_plan_s {
     bool has_filter = false;
     // split path (N > 16384)
     float2 *tw_top = nullptr;     // W_N^{q k0}, k0 = 0 .. RT-1
-    float2 *scratch = nullptr;    // chunk_blocks * N sub-results
-    int64_t chunk_blocks = 0;
+    float2 *scratch = nullptr;    // max_groups slots of N values
 };
 
 namespace {
@@ -46,13 +44,13 @@ bool on_plan_device(const fir_ols_plan_s *p) {
 }
 
 void release(fir_ols_plan_s *p) {
-    hipFree(p->tw_top);
-    hipFree(p->scratch);
-    hipFree(p->H);
-    hipFree(p->tw);
-    hipFree(p->taps);
-    hipFree(p->state[0]);
-    hipFree(p->state[1]);
+    (void)hipFree(p->tw_top);
+    (void)hipFree(p->scratch);
+    (void)hipFree(p->H);
+    (void)hipFree(p->tw);
+    (void)hipFree(p->taps);
+    (void)hipFree(p->state[0]);
+    (void)hipFree(p->state[1]);
     delete p;
 }
 
@@ -63,19 +61,6 @@ bool is_big(const fir_ols_plan_s *p) { return p->logn == firols::kBigLogN; }
 // geometry id of the plan's table builders (fused and half-resident paths)
 int table_geometry(const fir_ols_plan_s *p) {
     return is_big(p) ? firols::big_geometry() : p->logn;
-}
-
-// Scratch of the split path: enough blocks per chunk to keep every CU busy,
-// small enough (128 MiB by default) to stay in the 256 MB last-level cache.
-int64_t split_chunk_blocks(int logn) {
-    int64_t mib = 128;
-    if (const char *e = std::getenv("FIR_OLS_SPLIT_SCRATCH_MIB")) {
-        const long v = std::strtol(e, nullptr, 10);
-        if (v >= 1 && v <= 65536) mib = v;
-    }
-    const int64_t per_block = firols::split_block_elems(logn) * (int64_t)sizeof(float2);
-    const int64_t n = (mib << 20) / per_block;
-    return n > 0 ? n : 1;
 }
 
 }  // namespace
@@ -110,7 +95,6 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
 
     const int ntw = split ? firols::split_sub_twiddle_count() : firols::twiddle_count(table_geometry(p));
     const int64_t ntop = split ? firols::split_top_twiddle_count(logn) : 0;
-    if (split) p->chunk_blocks = split_chunk_blocks(logn);
     const size_t sbytes = (size_t)state_len(p) * sizeof(float2);
     bool ok = hipMalloc(&p->H, N * sizeof(float2)) == hipSuccess &&
               hipMalloc(&p->tw, (size_t)(ntw > 0 ? ntw : 1) * sizeof(float2)) == hipSuccess &&
@@ -121,7 +105,8 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
     }
     if (ok && split) {
         ok = hipMalloc(&p->tw_top, (size_t)ntop * sizeof(float2)) == hipSuccess &&
-             hipMalloc(&p->scratch, (size_t)(p->chunk_blocks * N) * sizeof(float2)) == hipSuccess;
+             hipMalloc(&p->scratch, (size_t)p->max_groups * (size_t)firols::split_slot_elems(logn) *
+                                        sizeof(float2)) == hipSuccess;
     }
     if (!ok) {
         (void)hipGetLastError();
@@ -225,12 +210,7 @@ int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev, int64_t ns
         a.M = (int)p->M;
         a.L = (int)p->L;
         a.nchan = (int)p->nchan;
-        const int64_t total = nblk * p->nchan;
-        for (int64_t b = 0; b < total && e == hipSuccess; b += p->chunk_blocks) {
-            a.blk0 = b;
-            a.nchunk = total - b < p->chunk_blocks ? total - b : p->chunk_blocks;
-            e = firols::launch_split(p->logn, a, p->max_groups, (hipStream_t)stream);
-        }
+        e = firols::launch_split(p->logn, a, p->max_groups, (hipStream_t)stream);
     } else {
         firols::FusedArgs a;
         a.x = (const float2 *)x_dev;

@@ -77,19 +77,19 @@ def _large_cases():
     return cases
 
 
-@pytest.mark.parametrize("N,M,n,nchan,seed", [
-    pytest.param(*c, marks=SKIP_TAPS_65536) if c[0] == 65536 else c for c in _large_cases()])
-def test_large_sizes_small_chunks(N, M, n, nchan, seed, monkeypatch):
-    # a 1 MiB scratch forces a chunk of one or two blocks, so every call
-    # crosses many chunk boundaries
-    monkeypatch.setenv("FIR_OLS_SPLIT_SCRATCH_MIB", "1")
+@pytest.mark.parametrize("N,M,n,nchan,seed", _large_cases())
+def test_large_sizes(N, M, n, nchan, seed):
+    # N = 65536 takes its filter as H (set_taps is refused at that size)
     say(f"large: N={N} M={M} n={n} nchan={nchan} seed={seed}")
     rng = np.random.default_rng(seed)
     h = (rng.standard_normal(M) + 1j * rng.standard_normal(M)).astype(np.complex64)
     x = W.complex_normal(rng, (nchan, n))
     s0 = W.complex_normal(rng, (nchan, M - 1))
     with fo.Plan(M, N, nchan) as p:
-        p.set_taps(h)
+        if N == 65536:
+            p.set_freq_response(W.freq_response_input(h, N))
+        else:
+            p.set_taps(h)
         y = run_calls(p, x, [n], s0=s0)
         st = p.get_state().cpu().numpy()
     idx = np.unique(np.concatenate([np.arange(min(n, 3000)), np.arange(max(0, n - 3000), n),
@@ -134,16 +134,18 @@ def test_large_delay_response(N, M, d):
     check(y, want.astype(np.complex128), np.ones(1), x, s0, "delay")
 
 
-@SKIP_TAPS_65536
-def test_large_repeat_is_bitwise_identical():
-    say("large determinism")
+@pytest.mark.parametrize("N,M", [(32768, 8193), (65536, 16385)])
+def test_large_repeat_is_bitwise_identical(N, M):
+    say(f"large determinism: N={N} M={M}")
     rng = np.random.default_rng(3)
-    M, N = 16385, 65536
     h = rng.standard_normal(M).astype(np.float32)
     x = W.complex_normal(rng, (1, 400000))
     outs = []
     for _ in range(2):
         with fo.Plan(M, N) as p:
-            p.set_taps(h)
+            if N == 65536:
+                p.set_freq_response(W.freq_response_input(h, N))
+            else:
+                p.set_taps(h)
             outs.append(run_calls(p, x, [123457, 276543]))
     np.testing.assert_array_equal(outs[0], outs[1])
