@@ -57,6 +57,8 @@ void build_twiddles(int gid, float2 *host_out);
 // perm[i]: the spectrum bin whose value the kernels expect at H[i].
 void build_h_permutation(int gid, int64_t *perm);
 
+// Geometry id of the fused kernel for a transform of 2^logn points.
+int fused_geometry(int logn);
 // Workgroups of the filtering kernel that fit on the device at once
 // (resident workgroups per CU times CUs); the kernel is persistent and
 // never launches more.

@@ -144,9 +144,11 @@ __device__ __forceinline__ void load_pass0_twiddles(float2 (&w)[N], const TW &tw
 
 // Passes 1 and 2 (forward), the product with H and inverse passes 2 and 1
 // of virtual thread H, on the half of the block that LDS holds.
-template <int H, class TW>
+// pre() runs before the half's last barrier, when its working registers
+// are free (the caller requests loads it needs right after the half).
+template <int H, class TW, class PRE>
 __device__ __forceinline__ void big_half(int tb, float2 *lds, const TW &tw,
-                                         __amdgpu_buffer_rsrc_t Hp) {
+                                         __amdgpu_buffer_rsrc_t Hp, const PRE &pre) {
     float2 c[32];
     get_run<33>(lds + slot1(tb), c);
     fwd_vt<1, H>(c, tw);
@@ -173,6 +175,9 @@ __device__ __forceinline__ void big_half(int tb, float2 *lds, const TW &tw,
     get_run<33>(lds + slot1(tb), c);
     inv_vt<1, H>(c, tw);
     put_run<33>(lds + slot1(tb), c);
+    __builtin_amdgcn_sched_barrier(0);
+    pre();
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
 }
 
@@ -196,35 +201,45 @@ __device__ __forceinline__ void big_transform(int tb, float2 (&a)[64], float2 (&
     fwd_pass0_first<1>(a, w1);
     put0<1, 0>(tb, a, lds);
     __syncthreads();
-    big_half<0>(tb, lds, tw, Hp);
-    // registers k < 16 take the first half's results back (conjugate
-    // twiddles applied); the second half's forward twiddles follow
+    // the second half's forward twiddles are requested at the end of the
+    // first half, the conjugate twiddles of virtual thread 0 at the end of
+    // the second; the first half's results wait untwiddled in registers
+    // k < 16 until the last DFT
+    float2 wf0[16], wf1[16];
+    big_half<0>(tb, lds, tw, Hp, [&] {
+        load_pass0_twiddles<0, 16>(wf0, tw);
+        load_pass0_twiddles<1, 16>(wf1, tw);
+    });
     get0<0, 0>(tb, a, lds);
-    pass0_twiddles<0, 0, 16, true>(a, tw);
     get0<1, 0>(tb, a, lds);
-    pass0_twiddles<1, 0, 16, true>(a, tw);
-    pass0_twiddles<0, 16, 32, false>(a, tw);
-    pass0_twiddles<1, 16, 32, false>(a, tw);
+    static_for<16, 32>([&](auto Kk) {
+        constexpr int k = decltype(Kk)::value;
+        a[k] = cmul(a[k], wf0[k - 16]);
+        a[32 + k] = cmul(a[32 + k], wf1[k - 16]);
+    });
     __syncthreads();
     put0<0, 1>(tb, a, lds);
     put0<1, 1>(tb, a, lds);
     __syncthreads();
-    big_half<1>(tb, lds, tw, Hp);
+    float2 wc[31];
+    big_half<1>(tb, lds, tw, Hp, [&] { load_pass0_twiddles<0, 1>(wc, tw); });
     get0<0, 1>(tb, a, lds);
-    pass0_twiddles<0, 16, 32, true>(a, tw);
+    static_for<1, 32>([&](auto Kk) {
+        constexpr int k = decltype(Kk)::value;
+        a[k] = cmulc(a[k], wc[k - 1]);
+    });
     dft_at<32, 1, 0>(a);
     // virtual thread 1's twiddles come before the stores and the next
     // block's input
     __builtin_amdgcn_sched_barrier(0);
-    float2 wi[16];
-    load_pass0_twiddles<1, 16>(wi, tw);
+    load_pass0_twiddles<1, 1>(wc, tw);
     __builtin_amdgcn_sched_barrier(0);
     out(ic<0>{}, a);
     next(ic<0>{}, a);
     get0<1, 1>(tb, a, lds);
-    static_for<16, 32>([&](auto Kk) {
+    static_for<1, 32>([&](auto Kk) {
         constexpr int k = decltype(Kk)::value;
-        a[32 + k] = cmulc(a[32 + k], wi[k - 16]);
+        a[32 + k] = cmulc(a[32 + k], wc[k - 1]);
     });
     dft_at<32, 1, 32>(a);
     __builtin_amdgcn_sched_barrier(0);

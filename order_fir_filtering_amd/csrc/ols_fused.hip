@@ -201,6 +201,11 @@ __global__ __launch_bounds__(256) void copy_kernel(float2 *__restrict__ dst,
         dst[k] = src ? src[k] : make_float2(0.f, 0.f);
 }
 
+// Geometry of the fused kernel for each transform size (geometry.hpp).
+constexpr int fused_gid(int logn) { return logn; }
+
+int fused_geometry(int logn) { return fused_gid(logn); }
+
 template <int GID>
 static hipError_t launch_fused_t(const FusedArgs &a, int max_groups, hipStream_t stream) {
     using C = FusedCfg<GID>;
@@ -224,18 +229,18 @@ static hipError_t launch_plan_t(const float2 *taps, float2 *H, const float2 *tw,
 
 hipError_t launch_fused(int logn, const FusedArgs &a, int max_groups, hipStream_t stream) {
     switch (logn) {
-        case 3: return launch_fused_t<3>(a, max_groups, stream);
-        case 4: return launch_fused_t<4>(a, max_groups, stream);
-        case 5: return launch_fused_t<5>(a, max_groups, stream);
-        case 6: return launch_fused_t<6>(a, max_groups, stream);
-        case 7: return launch_fused_t<7>(a, max_groups, stream);
-        case 8: return launch_fused_t<8>(a, max_groups, stream);
-        case 9: return launch_fused_t<9>(a, max_groups, stream);
-        case 10: return launch_fused_t<10>(a, max_groups, stream);
-        case 11: return launch_fused_t<11>(a, max_groups, stream);
-        case 12: return launch_fused_t<12>(a, max_groups, stream);
-        case 13: return launch_fused_t<13>(a, max_groups, stream);
-        case 14: return launch_fused_t<14>(a, max_groups, stream);
+        case 3: return launch_fused_t<fused_gid(3)>(a, max_groups, stream);
+        case 4: return launch_fused_t<fused_gid(4)>(a, max_groups, stream);
+        case 5: return launch_fused_t<fused_gid(5)>(a, max_groups, stream);
+        case 6: return launch_fused_t<fused_gid(6)>(a, max_groups, stream);
+        case 7: return launch_fused_t<fused_gid(7)>(a, max_groups, stream);
+        case 8: return launch_fused_t<fused_gid(8)>(a, max_groups, stream);
+        case 9: return launch_fused_t<fused_gid(9)>(a, max_groups, stream);
+        case 10: return launch_fused_t<fused_gid(10)>(a, max_groups, stream);
+        case 11: return launch_fused_t<fused_gid(11)>(a, max_groups, stream);
+        case 12: return launch_fused_t<fused_gid(12)>(a, max_groups, stream);
+        case 13: return launch_fused_t<fused_gid(13)>(a, max_groups, stream);
+        case 14: return launch_fused_t<fused_gid(14)>(a, max_groups, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -256,18 +261,18 @@ int fused_max_groups(int logn, int device) {
         cus < 1)
         cus = 1;
     switch (logn) {
-        case 3: return max_groups_t<3>(cus);
-        case 4: return max_groups_t<4>(cus);
-        case 5: return max_groups_t<5>(cus);
-        case 6: return max_groups_t<6>(cus);
-        case 7: return max_groups_t<7>(cus);
-        case 8: return max_groups_t<8>(cus);
-        case 9: return max_groups_t<9>(cus);
-        case 10: return max_groups_t<10>(cus);
-        case 11: return max_groups_t<11>(cus);
-        case 12: return max_groups_t<12>(cus);
-        case 13: return max_groups_t<13>(cus);
-        case 14: return max_groups_t<14>(cus);
+        case 3: return max_groups_t<fused_gid(3)>(cus);
+        case 4: return max_groups_t<fused_gid(4)>(cus);
+        case 5: return max_groups_t<fused_gid(5)>(cus);
+        case 6: return max_groups_t<fused_gid(6)>(cus);
+        case 7: return max_groups_t<fused_gid(7)>(cus);
+        case 8: return max_groups_t<fused_gid(8)>(cus);
+        case 9: return max_groups_t<fused_gid(9)>(cus);
+        case 10: return max_groups_t<fused_gid(10)>(cus);
+        case 11: return max_groups_t<fused_gid(11)>(cus);
+        case 12: return max_groups_t<fused_gid(12)>(cus);
+        case 13: return max_groups_t<fused_gid(13)>(cus);
+        case 14: return max_groups_t<fused_gid(14)>(cus);
         default: return cus;
     }
 }
@@ -275,18 +280,18 @@ int fused_max_groups(int logn, int device) {
 hipError_t launch_plan_taps(int logn, const float2 *taps, float2 *H, const float2 *tw,
                             hipStream_t stream) {
     switch (logn) {
-        case 3: return launch_plan_t<3>(taps, H, tw, stream);
-        case 4: return launch_plan_t<4>(taps, H, tw, stream);
-        case 5: return launch_plan_t<5>(taps, H, tw, stream);
-        case 6: return launch_plan_t<6>(taps, H, tw, stream);
-        case 7: return launch_plan_t<7>(taps, H, tw, stream);
-        case 8: return launch_plan_t<8>(taps, H, tw, stream);
-        case 9: return launch_plan_t<9>(taps, H, tw, stream);
-        case 10: return launch_plan_t<10>(taps, H, tw, stream);
-        case 11: return launch_plan_t<11>(taps, H, tw, stream);
-        case 12: return launch_plan_t<12>(taps, H, tw, stream);
-        case 13: return launch_plan_t<13>(taps, H, tw, stream);
-        case 14: return launch_plan_t<14>(taps, H, tw, stream);
+        case 3: return launch_plan_t<fused_gid(3)>(taps, H, tw, stream);
+        case 4: return launch_plan_t<fused_gid(4)>(taps, H, tw, stream);
+        case 5: return launch_plan_t<fused_gid(5)>(taps, H, tw, stream);
+        case 6: return launch_plan_t<fused_gid(6)>(taps, H, tw, stream);
+        case 7: return launch_plan_t<fused_gid(7)>(taps, H, tw, stream);
+        case 8: return launch_plan_t<fused_gid(8)>(taps, H, tw, stream);
+        case 9: return launch_plan_t<fused_gid(9)>(taps, H, tw, stream);
+        case 10: return launch_plan_t<fused_gid(10)>(taps, H, tw, stream);
+        case 11: return launch_plan_t<fused_gid(11)>(taps, H, tw, stream);
+        case 12: return launch_plan_t<fused_gid(12)>(taps, H, tw, stream);
+        case 13: return launch_plan_t<fused_gid(13)>(taps, H, tw, stream);
+        case 14: return launch_plan_t<fused_gid(14)>(taps, H, tw, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -60,7 +60,7 @@ bool is_split(const fir_ols_plan_s *p) { return p->logn > firols::kBigLogN; }
 bool is_big(const fir_ols_plan_s *p) { return p->logn == firols::kBigLogN; }
 // geometry id of the plan's table builders (fused and half-resident paths)
 int table_geometry(const fir_ols_plan_s *p) {
-    return is_big(p) ? firols::big_geometry() : p->logn;
+    return is_big(p) ? firols::big_geometry() : firols::fused_geometry(p->logn);
 }
 
 }  // namespace
