@@ -66,7 +66,9 @@ enum {
  *          its own state.
  * Allocates the frequency response (aligned to 256 bytes, the page's
  * alignment rule in step 1), the twiddle tables and two state buffers of
- * nchan*(M-1) samples on the current device.  The state starts at zero.
+ * nchan*(M-1) samples on the current device; for N = 65536 also a scratch
+ * area of N samples (512 KB) per workgroup that fits on the device at once
+ * (128 MiB on a 256-CU MI355X).  The state starts at zero.
  * No filter is set yet.  Synchronous.
  */
 int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan);

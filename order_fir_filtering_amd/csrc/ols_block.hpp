@@ -88,10 +88,6 @@ __device__ __forceinline__ float2 buf_load_cached(__amdgpu_buffer_rsrc_t r, uint
 // gfx950): the outputs are not read again, and streaming them out during
 // the kernel leaves fewer dirty L2 lines to write back when it ends.
 constexpr int kStoreNT = 2;
-typedef float nt_float2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void nt_store(float2 *p, float2 v) {
-    __builtin_nontemporal_store(nt_float2{v.x, v.y}, reinterpret_cast<nt_float2 *>(p));
-}
 __device__ __forceinline__ void buf_store(float2 v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(decltype(
         __builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, voff, 0, kStoreNT);
@@ -103,14 +99,6 @@ __device__ __forceinline__ void buf_store_cached(float2 v, __amdgpu_buffer_rsrc_
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(decltype(
         __builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, voff, soff, 0);
 }
-// The same with a scalar offset, for stores that are all in range (the
-// range check is not relied on, so the constant part may sit in soff).
-__device__ __forceinline__ void buf_store_so(float2 v, __amdgpu_buffer_rsrc_t r, uint32_t voff,
-                                             uint32_t soff) {
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(decltype(
-        __builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, voff, soff, kStoreNT);
-}
-
 // State carry: the last M-1 samples of {S0, x} of channel c go to the new
 // state buffer (TB threads of the block that ends the channel).
 template <int GID>

@@ -85,87 +85,6 @@ struct TwRegs {
     }
 };
 
-// Twiddle provider holding fewer registers: in a pass whose virtual
-// threads u = 0 .. V-1 stay inside one sub-transform (S >= TB * V, so
-// t_u = t_0 + TB u), W_{S R}^{t_u k} = W_{S R}^{t_0 k} * W_{S R}^{TB u k}; the
-// second factor is a constant rotation by a multiple of pi/16 when
-// 32 TB / (S R) is a whole number, and only the u = 0 values are kept.
-template <int GID>
-struct TwRegsCompact {
-    static constexpr Geo G = make_geo(GID);
-    static constexpr bool compact(int s) {
-        return s < G.npass - 1 && G.P / G.R[s] > 1 && G.S[s] >= G.TB * (G.P / G.R[s]) &&
-               (32 * G.TB) % (G.S[s] * G.R[s]) == 0;
-    }
-    static constexpr int kept(int s) {
-        return compact(s) ? G.R[s] - 1 : (G.P / G.R[s]) * (G.R[s] - 1);
-    }
-    static constexpr int off(int s) {
-        int o = 0;
-        for (int i = 0; i < s && i < G.npass - 1; ++i) o += kept(i);
-        return o;
-    }
-    static constexpr int count() { return off(G.npass - 1) > 0 ? off(G.npass - 1) : 1; }
-    float2 w[count()];
-    __host__ __device__ __forceinline__ void load(const float2 *__restrict__ tw, int tb) {
-        static_for<0, G.npass - 1>([&](auto Sx) {
-            constexpr int s = decltype(Sx)::value;
-            constexpr int R = G.R[s], V = compact(s) ? 1 : G.P / R;
-            static_for<0, V>([&](auto U) {
-                constexpr int u = decltype(U)::value;
-                const int t = pass_t<GID, s>(tb, u);
-                static_for<1, R>([&](auto Kk) {
-                    constexpr int k = decltype(Kk)::value;
-                    w[off(s) + u * (R - 1) + k - 1] = tw[G.twoff[s] + (k - 1) * G.S[s] + t];
-                });
-            });
-        });
-    }
-    template <int SI, int U, int K>
-    __host__ __device__ __forceinline__ float2 operator()(ic<SI>, ic<U>, ic<K>) const {
-        constexpr int R = G.R[SI];
-        if constexpr (compact(SI)) {
-            constexpr int unit = (32 * G.TB) / (G.S[SI] * G.R[SI]);   // pi/16 steps per TB
-            return rot32<-(U * K * unit)>(w[off(SI) + K - 1]);
-        } else {
-            return w[off(SI) + U * (R - 1) + K - 1];
-        }
-    }
-};
-
-// Twiddle provider for three-pass transforms whose pass 0 is compact (see
-// TwRegsCompact): pass 0 from R0-1 registers plus constant rotations, pass 1
-// from a copy of its table in LDS (S1 * (R1 - 1) values, [k-1][t] order).
-template <int GID>
-struct TwRegLds {
-    static constexpr Geo G = make_geo(GID);
-    static_assert(G.npass == 3 && TwRegsCompact<GID>::compact(0), "three passes, compact pass 0");
-    static constexpr int lds_count = G.S[1] * (G.R[1] - 1);
-    float2 w0[G.R[0] - 1];
-    const float2 *lds_tw;
-    int tb;
-    // registers of pass 0; the LDS table is filled by fill_lds
-    __host__ __device__ __forceinline__ void load(const float2 *__restrict__ tw, const float2 *lt,
-                                                  int t_b) {
-        tb = t_b;
-        lds_tw = lt;
-        const int t = pass_t<GID, 0>(tb, 0);
-        static_for<1, G.R[0]>([&](auto Kk) {
-            constexpr int k = decltype(Kk)::value;
-            w0[k - 1] = tw[G.twoff[0] + (k - 1) * G.S[0] + t];
-        });
-    }
-    template <int SI, int U, int K>
-    __host__ __device__ __forceinline__ float2 operator()(ic<SI>, ic<U>, ic<K>) const {
-        if constexpr (SI == 0) {
-            constexpr int unit = (32 * G.TB) / (G.S[0] * G.R[0]);
-            return rot32<-(U * K * unit)>(w0[K - 1]);
-        } else {
-            return lds_tw[(K - 1) * G.S[1] + pass_t<GID, 1>(tb, U)];
-        }
-    }
-};
-
 // H provider reading the plan's H (kernel order: H[r * TB + tb]).
 template <int GID>
 struct HTable {
