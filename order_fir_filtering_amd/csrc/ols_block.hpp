@@ -12,6 +12,21 @@
 
 namespace firols {
 
+// Barrier of an LDS exchange.  A block of at most 64 threads lies inside
+// one wave, and a wave's LDS operations execute in order, so its exchange
+// needs only a wave-level barrier (which keeps the compiler from moving
+// LDS accesses across it); larger blocks need the workgroup barrier.
+template <int GID>
+__device__ __forceinline__ void block_sync() {
+    if constexpr (make_geo(GID).TB <= 64) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+        __syncthreads();
+    }
+}
+
 // Forward passes with LDS exchanges between them.
 template <int GID, class TW>
 __device__ __forceinline__ void forward_all(int tb, float2 (&a)[make_geo(GID).P],
@@ -20,9 +35,9 @@ __device__ __forceinline__ void forward_all(int tb, float2 (&a)[make_geo(GID).P]
     static_for<0, G.npass>([&](auto Sx) {
         constexpr int s = decltype(Sx)::value;
         if constexpr (s > 0) {
-            __syncthreads();
+            block_sync<GID>();
             lds_put<GID, s - 1>(tb, a, lds);
-            __syncthreads();
+            block_sync<GID>();
             lds_get<GID, s>(tb, a, lds);
         }
         fwd_pass<GID, s>(a, tw);
@@ -37,9 +52,9 @@ __device__ __forceinline__ void inverse_all(int tb, float2 (&a)[make_geo(GID).P]
     static_for<0, G.npass>([&](auto Ix) {
         constexpr int s = G.npass - 1 - decltype(Ix)::value;
         if constexpr (s < G.npass - 1) {
-            __syncthreads();
+            block_sync<GID>();
             lds_put<GID, s + 1>(tb, a, lds);
-            __syncthreads();
+            block_sync<GID>();
             lds_get<GID, s>(tb, a, lds);
         }
         inv_pass<GID, s>(a, tw);
