@@ -121,6 +121,12 @@ int fir_ols_set_freq_response(fir_ols_plan_t p, const float *H_host,
  * overlap (in-place filtering would let one block overwrite the overlap
  * another block still reads).  The state of every channel becomes the last
  * M-1 samples of {S0, x} of that channel.
+ * The call enqueues kernel launches only (no allocation, copy, fill or
+ * synchronization), so a run of calls may be captured into a HIP graph;
+ * replays then carry the state like the calls they were captured from,
+ * provided the captured run has an even number of calls with M > 1 (the
+ * two state buffers alternate, and the plan's record of which one is
+ * current changes at capture time, not at replay).
  */
 int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev,
                     int64_t nsamples, int64_t chan_stride, void *stream);
