@@ -149,6 +149,10 @@ __device__ __forceinline__ void load_pass0_twiddles(float2 (&w)[N], const TW &tw
 template <int H, class TW, class PRE>
 __device__ __forceinline__ void big_half(int tb, float2 *lds, const TW &tw,
                                          __amdgpu_buffer_rsrc_t Hp, const PRE &pre) {
+    // Sub-transform K of the half belongs to the 32 threads tb / 32 = K, and
+    // its pass-1 and pass-2 slots both lie in [1056 K, 1056 K + 1056): the
+    // exchanges between passes 1 and 2 stay inside half a wave, so a wave
+    // barrier orders them and the waves run this part independently.
     float2 c[32];
     get_run<33>(lds + slot1(tb), c);
     fwd_vt<1, H>(c, tw);
@@ -162,7 +166,7 @@ __device__ __forceinline__ void big_half(int tb, float2 *lds, const TW &tw,
         hv[k] = buf_load_cached(Hp, (uint32_t)tb * 8u, (uint32_t)(32 * H + k) * kBig.TB * 8u);
     });
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    wave_sync();
     get_run<1>(lds + slot2(tb), c);
     fwd_vt<2, H>(c, tw);
     static_for<0, 32>([&](auto Kk) {
@@ -171,7 +175,7 @@ __device__ __forceinline__ void big_half(int tb, float2 *lds, const TW &tw,
     });
     inv_vt<2, H>(c, tw);
     put_run<1>(lds + slot2(tb), c);
-    __syncthreads();
+    wave_sync();
     get_run<33>(lds + slot1(tb), c);
     inv_vt<1, H>(c, tw);
     put_run<33>(lds + slot1(tb), c);

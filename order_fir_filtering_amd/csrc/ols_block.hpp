@@ -16,15 +16,17 @@ namespace firols {
 // one wave, and a wave's LDS operations execute in order, so its exchange
 // needs only a wave-level barrier (which keeps the compiler from moving
 // LDS accesses across it); larger blocks need the workgroup barrier.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 template <int GID>
 __device__ __forceinline__ void block_sync() {
-    if constexpr (make_geo(GID).TB <= 64) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    } else {
+    if constexpr (make_geo(GID).TB <= 64)
+        wave_sync();
+    else
         __syncthreads();
-    }
 }
 
 // Forward passes with LDS exchanges between them.
