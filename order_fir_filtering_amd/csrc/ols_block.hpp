@@ -29,6 +29,22 @@ __device__ __forceinline__ void block_sync() {
         __syncthreads();
 }
 
+// Barrier of the exchange between passes s-1 and s.  When both passes
+// have one virtual thread per thread and the same radix, the positions
+// pass s reads of one sub-block of S[s-1] points were all written by the
+// S[s-1] consecutive threads that own that sub-block, so with S[s-1] <= 64
+// the exchange stays inside a wave.
+template <int GID, int SI>
+__device__ __forceinline__ void exchange_sync() {
+    constexpr Geo G = make_geo(GID);
+    constexpr bool local = G.TB <= 64 ||
+                           (G.R[SI - 1] == G.P && G.R[SI] == G.P && G.S[SI - 1] <= 64);
+    if constexpr (local)
+        wave_sync();
+    else
+        __syncthreads();
+}
+
 // Forward passes with LDS exchanges between them.
 template <int GID, class TW>
 __device__ __forceinline__ void forward_all(int tb, float2 (&a)[make_geo(GID).P],
@@ -39,7 +55,7 @@ __device__ __forceinline__ void forward_all(int tb, float2 (&a)[make_geo(GID).P]
         if constexpr (s > 0) {
             block_sync<GID>();
             lds_put<GID, s - 1>(tb, a, lds);
-            block_sync<GID>();
+            exchange_sync<GID, s>();
             lds_get<GID, s>(tb, a, lds);
         }
         fwd_pass<GID, s>(a, tw);
@@ -56,7 +72,7 @@ __device__ __forceinline__ void inverse_all(int tb, float2 (&a)[make_geo(GID).P]
         if constexpr (s < G.npass - 1) {
             block_sync<GID>();
             lds_put<GID, s + 1>(tb, a, lds);
-            block_sync<GID>();
+            exchange_sync<GID, s + 1>();
             lds_get<GID, s>(tb, a, lds);
         }
         inv_pass<GID, s>(a, tw);
