@@ -159,6 +159,22 @@ __host__ __device__ __forceinline__ void dft(float2 (&a)[R]) {
     }
 }
 
+// The order in which dft<R> first needs its inputs: the first stage of
+// dft_split<R1, R2> takes a[R2 j1 + j2] for j1 = 0 .. R1-1, one j2 after
+// the other.  Loads issued in this order complete in this order, so the
+// first butterflies can start before the last input arrives.
+template <int R>
+__host__ __device__ constexpr int dft_input_order(int i) {
+    if constexpr (R == 8)
+        return 4 * (i % 2) + i / 2;
+    else if constexpr (R == 16)
+        return 4 * (i % 4) + i / 4;
+    else if constexpr (R == 32)
+        return 8 * (i % 4) + i / 4;
+    else
+        return i;
+}
+
 // R-point DFT on a[OFF .. OFF+R) of a larger register array.
 template <int R, int DIR, int OFF, int P>
 __host__ __device__ __forceinline__ void dft_at(float2 (&a)[P]) {

@@ -83,7 +83,10 @@ __device__ __forceinline__ void put_run(float2 *p, const float2 (&c)[32]) {
 }
 template <int STEP>
 __device__ __forceinline__ void get_run(const float2 *p, float2 (&c)[32]) {
-    static_for<0, 32>([&](auto J) { c[decltype(J)::value] = p[STEP * decltype(J)::value]; });
+    static_for<0, 32>([&](auto I) {
+        constexpr int j = dft_input_order<32>(decltype(I)::value);
+        c[j] = p[STEP * j];
+    });
 }
 
 // Forward / inverse radix-32 pass SI of virtual thread U on 32 registers.

@@ -184,7 +184,10 @@ __host__ __device__ __forceinline__ void lds_get(int tb, float2 (&a)[make_geo(GI
     static_for<0, V>([&](auto U) {
         constexpr int u = decltype(U)::value;
         const float2 *p = lds + lds_base<GID, SI>(tb + G.TB * u);
-        static_for<0, R>([&](auto J) { a[u * R + decltype(J)::value] = p[decltype(J)::value * st]; });
+        static_for<0, R>([&](auto I) {
+            constexpr int j = dft_input_order<R>(decltype(I)::value);
+            a[u * R + j] = p[j * st];
+        });
     });
 }
 
