@@ -1,8 +1,10 @@
-"""GPU parity of the large-N (split) path, N = 32768 and 65536.
+"""GPU parity of the large-N paths, N = 32768 and 65536.
 
-Full-size workloads are checked on sampled outputs the float64 oracle
-computes one by one: four whole blocks (first, second, middle, last) plus
-65536 seeded random indices.  Small cases cover every output.
+Full-size workloads are checked on sampled outputs the float64 direct-form
+oracle computes one by one (four whole blocks: first, second, middle,
+last, plus 65536 seeded random indices), and on every output against the
+oracle's float64 block overlap-save (numpy FFTs), which the CPU tests pin
+to the direct form.  Small cases cover every output with the direct form.
 """
 import os
 
@@ -15,9 +17,10 @@ import workloads as W
 from gpu_util import check, run_calls, say, to_dev
 
 pytestmark = pytest.mark.gpu
-# The first run of the N = 65536 taps transform (fir_ols_set_taps, 4-way
-# split) faulted the GPU with no cause found on the CPU; that entry point is
-# switched off for N = 65536 and its cases stay skipped until the cause is.
+# The first run of an earlier N = 65536 taps transform (fir_ols_set_taps)
+# faulted the GPU with no cause found on the CPU; that entry point is
+# switched off for N = 65536 and its one case stays skipped until the cause
+# is found.
 SKIP_TAPS_65536 = pytest.mark.skip(
     reason="set_taps at N=65536 is switched off after an unexplained GPU fault")
 THREADS = max(1, min(16, os.cpu_count() or 1))
@@ -51,6 +54,9 @@ def test_cfg3_sampled():
     ref = oracle.fir_direct(inp.h_ref, inp.x[0], inp.s0[0], idx=idx, threads=THREADS)
     check(y[0, idx], ref, inp.h_ref, inp.x, inp.s0, f"cfg3 ({idx.size} outputs)")
     np.testing.assert_array_equal(st[0], oracle.state_next(inp.x[0], inp.s0[0], w.M))
+    H = np.fft.fft(np.asarray(inp.h_ref, dtype=np.complex128), w.N)
+    full = oracle.fir_ols_blocks(H, inp.x[0], inp.s0[0], w.M)
+    check(y[0], full, inp.h_ref, inp.x, inp.s0, f"cfg3 (all {w.samples} outputs, block OLS)")
 
 
 def test_cfg4_frequency_response_sampled():
@@ -63,6 +69,8 @@ def test_cfg4_frequency_response_sampled():
     idx = sampled_indices(w, 44)
     ref = oracle.fir_direct(inp.h_ref, inp.x[0], inp.s0[0], idx=idx, threads=THREADS)
     check(y[0, idx], ref, inp.h_ref, inp.x, inp.s0, f"cfg4 ({idx.size} outputs)")
+    full = oracle.fir_ols_blocks(inp.H, inp.x[0], inp.s0[0], w.M)
+    check(y[0], full, inp.h_ref, inp.x, inp.s0, f"cfg4 (all {w.samples} outputs, block OLS)")
 
 
 def _large_cases():
