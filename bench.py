@@ -171,7 +171,7 @@ def cpu_baseline(inp, seconds_budget: float = 20.0):
     if want >= total:
         sample = f"all {total} outputs of the workload"
         reps, dt = 0, 0.0
-        while reps < 20 and (reps == 0 or dt < 2.0):
+        while reps < 100 and (reps == 0 or dt < 10.0):
             t0 = time.perf_counter()
             ref = oracle.fir_direct_multi(inp.h_ref, inp.x, inp.s0, threads=threads)
             dt += time.perf_counter() - t0
