@@ -112,8 +112,9 @@ __device__ __forceinline__ void inv_vt(float2 (&c)[32], const TW &tw) {
 // Pass 0 of virtual thread U is split by its output index k: the DFT and
 // the twiddles of k < 16 (the first half's outputs) come first, the
 // twiddles of k >= 16 only when the second half goes to LDS.  In the
-// inverse the conjugate twiddles of each half are applied as it returns,
-// and the DFT comes last.  This bounds the twiddles in flight at 16.
+// inverse all conjugate twiddles are applied just before the last DFT.
+// pass0_twiddles requests and applies the twiddles of outputs K0 .. K1-1
+// in one go (the taps planner's second-half twiddles).
 template <int U, int K0, int K1, bool CONJ, class TW>
 __device__ __forceinline__ void pass0_twiddles(float2 (&a)[64], const TW &tw) {
     __builtin_amdgcn_sched_barrier(0);
@@ -203,7 +204,7 @@ __device__ __forceinline__ void big_transform(int tb, float2 (&a)[64], float2 (&
     // forward pass 0; the first half's outputs go to LDS as soon as a
     // virtual thread is done
     fwd_pass0_first<0>(a, w0);
-    __syncthreads();                 // the previous block's readers of LDS are done
+    __syncthreads();                 // the previous block's LDS accesses are done
     put0<0, 0>(tb, a, lds);
     fwd_pass0_first<1>(a, w1);
     put0<1, 0>(tb, a, lds);
