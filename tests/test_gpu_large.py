@@ -157,3 +157,44 @@ def test_large_repeat_is_bitwise_identical(N, M):
                 p.set_taps(h)
             outs.append(run_calls(p, x, [123457, 276543]))
     np.testing.assert_array_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("N,M", [(32768, 4097), (65536, 20000)])
+def test_large_multichannel_padded_stride_streaming(N, M):
+    # three channels 77 elements apart beyond their length, fed as several
+    # calls (each call reads and writes a sub-range of every row)
+    import torch
+    say(f"large multichannel: N={N} M={M}")
+    rng = np.random.default_rng(N ^ M)
+    nchan, L = 3, N - M + 1
+    calls = [L + 11, 2, M - 5, 2 * L]
+    n = sum(calls)
+    stride = n + 77
+    h = W.complex_taps(rng, M).astype(np.complex64)
+    x = W.complex_normal(rng, (nchan, n))
+    s0 = W.complex_normal(rng, (nchan, M - 1))
+    xp = np.zeros((nchan, stride), np.complex64)
+    xp[:, :n] = x
+    xd = to_dev(xp)
+    yd = torch.full_like(xd, complex(7.0, -7.0))
+    with fo.Plan(M, N, nchan) as p:
+        if N == 65536:
+            p.set_freq_response(W.freq_response_input(h, N))
+        else:
+            p.set_taps(h)
+        p.set_state(to_dev(s0))
+        pos = 0
+        for c in calls:
+            fo.fir_ols_execute(p.handle, xd.data_ptr() + 8 * pos, yd.data_ptr() + 8 * pos, c,
+                               stride, None)
+            pos += c
+        torch.cuda.synchronize()
+        st = p.get_state().cpu().numpy()
+    y = yd.cpu().numpy()
+    # the padding between rows is untouched
+    assert np.all(y[:, n:] == np.complex64(complex(7.0, -7.0)))
+    idx = np.unique(np.concatenate([np.arange(0, n, 13), [n - 1]]))
+    ref = oracle.fir_direct_multi(h, x, s0, idx=idx, threads=THREADS)
+    check(y[:, idx], ref, h, x, s0, f"N={N} {nchan} channels, stride {stride}")
+    for c in range(nchan):
+        np.testing.assert_array_equal(st[c], oracle.state_next(x[c], s0[c], M))
