@@ -26,7 +26,7 @@ __global__ __launch_bounds__(kBig.TB) void ols_big_kernel(FusedArgs A) {
     int64_t gb = unit_of(units, blockIdx.x, gridDim.x, 0);
     float2 a[kBig.P], w0[15], w1[15];
     if (gb >= 0) {
-        gather_block_wave<kBigGid, true>(A, gb, tb, a);
+        gather_block_wave<kBigGid, true, false>(A, gb, tb, a);
         const TwBig tw0{buf_rsrc(A.tw, (uint32_t)kBig.twoff[kBig.npass] * 8u), lds_tw, tb};
         load_pass0_twiddles<0, 1>(w0, tw0);
         load_pass0_twiddles<1, 1>(w1, tw0);
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kBig.TB) void ols_big_kernel(FusedArgs A) {
             },
             [&](auto Uu, float2(&v)[64]) {
                 constexpr int u = decltype(Uu)::value;
-                if (gn >= 0) gather_block_wave<kBigGid, true, 32 * u, 32 * u + 32>(A, gn, tb, v);
+                if (gn >= 0) gather_block_wave<kBigGid, true, false, 32 * u, 32 * u + 32>(A, gn, tb, v);
             });
         if (i == A.nblk - 1)
             carry_state<kBigGid>(A.nsamples, Mm1, tb, A.x + c * A.stride, A.s0_old + c * Mm1,

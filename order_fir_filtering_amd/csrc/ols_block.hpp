@@ -106,16 +106,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uin
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                              0x00020000);
 }
-// Input loads also carry the non-temporal policy: each sample is read by
-// at most two neighbouring blocks close together in time.
+// Non-temporal load (cache-policy bit 1): for input that the small-block
+// kernel streams through once; the M-1 samples two neighbouring blocks
+// share are read by workgroups running side by side.
 __device__ __forceinline__ float2 buf_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 2));
 }
-// Loads of the plan's tables (twiddles, H), which every block reads again:
-// default cache policy.
+// Default-policy load: the plan's tables (twiddles, H), which every block
+// reads again, and the input of the large-block kernels, where the overlap
+// with the next block is read by the same workgroup one block later (the
+// non-temporal policy measured slower there).
 __device__ __forceinline__ float2 buf_load_cached(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                                   uint32_t soff) {
     return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+template <bool NT>
+__device__ __forceinline__ float2 buf_load_policy(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                  uint32_t soff) {
+    if constexpr (NT)
+        return buf_load(r, voff, soff);
+    else
+        return buf_load_cached(r, voff, soff);
 }
 // Output stores carry the non-temporal policy (cache-policy bit 1, NT on
 // gfx950): the outputs are not read again, and streaming them out during
@@ -154,8 +165,9 @@ __device__ __forceinline__ void carry_state(int64_t nsamples, int Mm1, int tb,
 // also gather through buffer descriptors (two range-checked loads per
 // point: one over the valid input, one over the state), which keeps the
 // per-point address registers of large P out of the kernel.
-// R0 .. R1 selects the registers to fill (default: all).
-template <int GID, bool BUF_EDGE = false, int R0 = 0, int R1 = make_geo(GID).P>
+// NT selects the input loads' cache policy; R0 .. R1 selects the
+// registers to fill (default: all).
+template <int GID, bool BUF_EDGE = false, bool NT = true, int R0 = 0, int R1 = make_geo(GID).P>
 __device__ __forceinline__ void gather_block_wave(const FusedArgs &A, int64_t gb, int tb,
                                                   float2 (&a)[make_geo(GID).P]) {
     constexpr Geo G = make_geo(GID);
@@ -174,7 +186,7 @@ __device__ __forceinline__ void gather_block_wave(const FusedArgs &A, int64_t gb
         const uint32_t vo = (uint32_t)tb * 8u;
         static_for<R0, R1>([&](auto Rr) {
             constexpr int r = decltype(Rr)::value;
-            a[r] = buf_load(rx, vo, (uint32_t)(G.TB * pass0_m<GID>(r) * 8));
+            a[r] = buf_load_policy<NT>(rx, vo, (uint32_t)(G.TB * pass0_m<GID>(r) * 8));
         });
     } else if constexpr (BUF_EDGE) {
         // first blocks (state in front) and the partial last block: the
@@ -190,8 +202,8 @@ __device__ __forceinline__ void gather_block_wave(const FusedArgs &A, int64_t gb
         const int ds = (int)(g0 + Mm1) + tb;    // q + ds indexes the state
         static_for<R0, R1>([&](auto Rr) {
             constexpr int off = G.TB * pass0_m<GID>(decltype(Rr)::value);
-            const float2 u = buf_load(rx, (uint32_t)(off + dx) * 8u, 0);
-            const float2 v = buf_load(rs, (uint32_t)(off + ds) * 8u, 0);
+            const float2 u = buf_load_policy<NT>(rx, (uint32_t)(off + dx) * 8u, 0);
+            const float2 v = buf_load_policy<NT>(rs, (uint32_t)(off + ds) * 8u, 0);
             a[decltype(Rr)::value] = make_float2(u.x + v.x, u.y + v.y);
         });
     } else {

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
         if (g0 >= 0 && g0 + kRT * kNs <= A.nsamples) {
             const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc + g0, (uint32_t)(kRT * kNs) * 8u);
             split_gather(a, tb, [&](int j, int off) {
-                return buf_load(rx, (uint32_t)tb * 8u, (uint32_t)(off + j * kNs) * 8u);
+                return buf_load_cached(rx, (uint32_t)tb * 8u, (uint32_t)(off + j * kNs) * 8u);
             }, rtt1, ra1);
         } else {
             // first blocks (state in front) and the partial last block: two
@@ -160,8 +160,8 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
             const int ds = (int)(g0 + Mm1) + tb;    // q + ds indexes the state
             split_gather(a, tb, [&](int j, int off) {
                 const int q = off + j * kNs;
-                const float2 u = buf_load(rx, (uint32_t)(q + dx) * 8u, 0);
-                const float2 v = buf_load(rs, (uint32_t)(q + ds) * 8u, 0);
+                const float2 u = buf_load_cached(rx, (uint32_t)(q + dx) * 8u, 0);
+                const float2 v = buf_load_cached(rs, (uint32_t)(q + ds) * 8u, 0);
                 return make_float2(u.x + v.x, u.y + v.y);
             }, rtt1, ra1);
         }
