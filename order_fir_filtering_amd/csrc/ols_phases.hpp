@@ -58,7 +58,12 @@ struct TwTable {
     }
 };
 
-// Twiddle provider holding this thread's twiddles in registers.
+// Twiddle provider holding this thread's twiddles in registers.  Only
+// the rows k = 2^b of the table are read; W^(t k) for any other k is the
+// product of the rows of k's set bits (k = (k & (k-1)) + lowest bit), so
+// each value carries at most log2 R table roundings and log2 R - 1
+// products.  A thread then reads log2 R instead of R - 1 values per pass,
+// and the products run while the block's input is still in flight.
 template <int GID>
 struct TwRegs {
     float2 w[thread_tw_count<GID>() > 0 ? thread_tw_count<GID>() : 1];
@@ -72,8 +77,21 @@ struct TwRegs {
                 const int t = pass_t<GID, s>(tb, u);
                 static_for<1, R>([&](auto Kk) {
                     constexpr int k = decltype(Kk)::value;
-                    w[thread_tw_off<GID>(s) + u * (R - 1) + k - 1] =
-                        tw[G.twoff[s] + (k - 1) * G.S[s] + t];
+                    if constexpr ((k & (k - 1)) == 0)
+                        w[thread_tw_off<GID>(s) + u * (R - 1) + k - 1] =
+                            tw[G.twoff[s] + (k - 1) * G.S[s] + t];
+                });
+            });
+        });
+        static_for<0, G.npass - 1>([&](auto Sx) {
+            constexpr int s = decltype(Sx)::value;
+            constexpr int R = G.R[s], V = G.P / R;
+            static_for<0, V>([&](auto U) {
+                constexpr int o = thread_tw_off<GID>(s) + decltype(U)::value * (R - 1) - 1;
+                static_for<1, R>([&](auto Kk) {
+                    constexpr int k = decltype(Kk)::value;
+                    if constexpr ((k & (k - 1)) != 0)
+                        w[o + k] = cmul(w[o + (k & (k - 1))], w[o + (k & -k)]);
                 });
             });
         });
