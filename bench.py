@@ -28,8 +28,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, AMD published figure
+VALU_PEAK_TFLOPS = 157.3          # MI355X fp32 vector, AMD published figure (packed fp32)
+VALU_PEAK_UNPACKED_TFLOPS = 78.6  # 256 CU x 4 SIMD x 16 lanes x 2 (FMA) x 2.4 GHz
+# one rocprofv3 --pmc pass (7 SQ counters; at most 8 fit one pass)
+VALU_COUNTERS = ("SQ_INSTS_VALU SQ_INSTS_VALU_ADD_F32 SQ_INSTS_VALU_MUL_F32 "
+                 "SQ_INSTS_VALU_FMA_F32 SQ_ACTIVE_INST_VALU SQ_BUSY_CYCLES SQ_WAVES")
 BYTES_PER_SAMPLE = 16             # complex64 in + complex64 out
 LLC_BYTES = 256 << 20             # MI355X Infinity Cache
+PROFILES_DIR = os.path.join(ROOT, "profiles")
 
 
 def parse():
@@ -49,7 +55,12 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="calibrate FETCH_SIZE / WRITE_SIZE runs of this script against "
                          "the copy kernel, write profiles/ summaries, then exit")
+    ap.add_argument("--summarize-valu", metavar="DIR",
+                    help="write profiles/ VALU summaries of a rocprofv3 --pmc run of this "
+                         "script with the counters of VALU_COUNTERS, then exit")
     ap.add_argument("--command", default="", help="command line recorded in the summary")
+    ap.add_argument("--profiles-dir", default="",
+                    help="where the summaries are written and read (default: profiles/)")
     return ap.parse_args()
 
 
@@ -71,9 +82,9 @@ def summarize_trace(args):
     rows = _csv_rows(args.summarize_trace, "kernel_stats.csv")
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     top = _short(rows[0]["Name"]).split("::")[-1].replace("<", "_").replace(">", "")
-    out = os.path.join(ROOT, "profiles", f"{top}_{args.workload}_kernel_trace.md")
+    out = os.path.join(PROFILES_DIR, f"{top}_{args.workload}_kernel_trace.md")
     lines = [f"# Kernel trace: {args.workload} ({WORKLOAD_NOTE.get(args.workload, '')})", "",
-             "Command (run from /tmp on the GPU box):", "", "```", args.command, "```", "",
+             "Command (working directory /tmp):", "", "```", args.command, "```", "",
              f"Kernel source hash: `{kernel_source_hash()}`", "",
              "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
              "|---|---|---|---|---|---|"]
@@ -114,7 +125,7 @@ def summarize_pmc(args):
     # per launch of the filtering call (all kernels of one call)
     per_launch = step_bytes  # counters are per dispatch; one dispatch per call
     alg = w.nchan * w.samples / calls * BYTES_PER_SAMPLE
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = os.path.join(PROFILES_DIR, "traffic.json")
     try:
         db = json.load(open(path))
     except (OSError, ValueError):
@@ -125,9 +136,9 @@ def summarize_pmc(args):
                          "write_scale": round(res["WRITE_SIZE"]["scale"], 4)}
     json.dump(db, open(path, "w"), indent=1, sort_keys=True)
     top = sorted(kernels)[0].split("::")[-1].replace("<", "_").replace(">", "")
-    out = os.path.join(ROOT, "profiles", f"{top}_{args.workload}_hbm_traffic.md")
+    out = os.path.join(PROFILES_DIR, f"{top}_{args.workload}_hbm_traffic.md")
     lines = [f"# HBM traffic: {args.workload} ({WORKLOAD_NOTE.get(args.workload, '')})", "",
-             "Two counter runs of the same command, one per counter (run from /tmp on the GPU box):",
+             "Two counter runs of the same command, one per counter (working directory /tmp):",
              "", "```", args.command, "```", "",
              f"Kernel source hash: `{kernel_source_hash()}`", "",
              "The counters are read per dispatch in KiB.  Each is scaled by the ratio of the true "
@@ -147,6 +158,73 @@ def summarize_pmc(args):
               f"Measured / algorithmic: {per_launch / alg:.3f}."]
     open(out, "w").write("\n".join(lines) + "\n")
     print(out)
+
+
+def summarize_valu(args):
+    """VALU instruction and fp32 flop counts per dispatch of the filtering
+    kernel, from one counter run; stored per workload in profiles/valu.json."""
+    import workloads as W
+    w = W.WORKLOADS[args.workload]
+    per = {}
+    for r in _csv_rows(args.summarize_valu, "counter_collection.csv"):
+        k = r["Kernel_Name"]
+        if "ols_" not in k or "plan_taps" in k:
+            continue
+        per.setdefault(_short(k), {}).setdefault(r["Counter_Name"], []).append(
+            float(r["Counter_Value"]))
+    if not per:
+        raise SystemExit(f"filtering kernel missing in {args.summarize_valu}")
+    names = VALU_COUNTERS.split()
+    kern = sorted(per)[0]
+    mean = {c: float(np.mean(per[kern][c])) for c in names if c in per[kern]}
+    missing = [c for c in names if c not in mean]
+    if missing:
+        raise SystemExit(f"counters missing: {missing}")
+    # wave-level instruction counts; every lane of the kernels' waves is active
+    flops = 64.0 * (mean["SQ_INSTS_VALU_ADD_F32"] + mean["SQ_INSTS_VALU_MUL_F32"]
+                    + 2.0 * mean["SQ_INSTS_VALU_FMA_F32"])
+    samples = w.nchan * w.samples / len(w.calls)
+    rec = {"kernel": kern, "source_hash": kernel_source_hash(),
+           "valu_instr_per_launch": mean["SQ_INSTS_VALU"],
+           "fp32_flops_per_launch": flops,
+           "valu_instr_per_sample": round(64.0 * mean["SQ_INSTS_VALU"] / samples, 2),
+           "fp32_flops_per_sample": round(flops / samples, 2),
+           "counters": {c: mean[c] for c in names}}
+    path = os.path.join(PROFILES_DIR, "valu.json")
+    try:
+        db = json.load(open(path))
+    except (OSError, ValueError):
+        db = {}
+    db[args.workload] = rec
+    json.dump(db, open(path, "w"), indent=1, sort_keys=True)
+    top = kern.split("::")[-1].replace("<", "_").replace(">", "")
+    out = os.path.join(PROFILES_DIR, f"{top}_{args.workload}_valu.md")
+    lines = [f"# VALU counters: {args.workload} ({WORKLOAD_NOTE.get(args.workload, '')})", "",
+             "One counter run (working directory /tmp):", "", "```", args.command, "```", "",
+             f"Kernel source hash: `{kernel_source_hash()}`", "",
+             f"Mean per dispatch of `{kern}` ({len(per[kern]['SQ_WAVES'])} dispatches):", "",
+             "| counter | value |", "|---|---|"]
+    for c in names:
+        lines.append(f"| {c} | {mean[c]:.6g} |")
+    lines += ["", f"fp32 flops per dispatch = 64 x (ADD_F32 + MUL_F32 + 2 FMA_F32) = {flops:.4g} "
+              f"({flops / samples:.1f} per output sample; VALU lane-instructions per output "
+              f"sample: {64.0 * mean['SQ_INSTS_VALU'] / samples:.1f}).  `bench.py` divides the "
+              "flops by the live per-launch duration for the VALU line of its output."]
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(out)
+
+
+def measured_valu(workload: str):
+    """The counter record of profiles/valu.json if it was taken with the
+    current kernel sources (else None)."""
+    path = os.path.join(PROFILES_DIR, "valu.json")
+    try:
+        rec = json.load(open(path)).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec
 
 
 def cpu_baseline(inp, seconds_budget: float = 20.0):
@@ -214,7 +292,7 @@ def kernel_source_hash() -> str:
 def measured_traffic(workload: str):
     """HBM bytes per launch from the committed counter summary, if it was
     taken with the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = os.path.join(PROFILES_DIR, "traffic.json")
     try:
         rec = json.load(open(path)).get(workload)
     except (OSError, ValueError):
@@ -222,6 +300,23 @@ def measured_traffic(workload: str):
     if not rec or rec.get("source_hash") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
+
+
+def valu_line(workload: str, kern_ms: float):
+    """fp32 VALU throughput of the filtering kernel: counted flops per
+    launch (committed counter run of the same sources) over the live
+    per-launch duration; None when the counters are stale."""
+    rec = measured_valu(workload)
+    if rec is None:
+        return None
+    tf = rec["fp32_flops_per_launch"] / (kern_ms * 1e-3) / 1e12
+    return {"achieved": round(tf, 2), "unit": "TFLOP/s", "peak": VALU_PEAK_TFLOPS,
+            "frac": round(tf / VALU_PEAK_TFLOPS, 4),
+            "peak_without_packed_fp32": VALU_PEAK_UNPACKED_TFLOPS,
+            "frac_without_packed_fp32": round(tf / VALU_PEAK_UNPACKED_TFLOPS, 4),
+            "fp32_flops_per_launch": rec["fp32_flops_per_launch"],
+            "fp32_flops_per_sample": rec["fp32_flops_per_sample"],
+            "valu_instr_per_sample": rec["valu_instr_per_sample"]}
 
 
 WORKLOAD_NOTE = {
@@ -235,11 +330,17 @@ WORKLOAD_NOTE = {
 
 def main():
     args = parse()
+    global PROFILES_DIR
+    if args.profiles_dir:
+        PROFILES_DIR = args.profiles_dir
     if args.summarize_trace:
         summarize_trace(args)
         return
     if args.summarize_pmc:
         summarize_pmc(args)
+        return
+    if args.summarize_valu:
+        summarize_valu(args)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -404,6 +505,7 @@ def main():
             "kernel_source_hash": kernel_source_hash(),
             "algorithmic_bytes_per_launch": int(kern_bytes),
         },
+        "valu": valu_line(w.key, kern_ms),
         "copy_reference_GBps": round(copy_gbps, 1),
         "parity": parity,
         "cpu_baseline": base,
