@@ -24,12 +24,12 @@ __global__ __launch_bounds__(kBig.TB) void ols_big_kernel(FusedArgs A) {
     // software-pipelined over blocks: the input of the next block is
     // requested as soon as the registers of a virtual thread are free
     int64_t gb = unit_of(units, blockIdx.x, gridDim.x, 0);
-    float2 a[kBig.P], w0[15], w1[15];
+    float2 a[kBig.P], r0[5], r1[5];
     if (gb >= 0) {
         gather_block_wave<kBigGid, true, false>(A, gb, tb, a);
         const TwBig tw0{buf_rsrc(A.tw, (uint32_t)kBig.twoff[kBig.npass] * 8u), lds_tw, tb};
-        load_pass0_twiddles<0, 1>(w0, tw0);
-        load_pass0_twiddles<1, 1>(w1, tw0);
+        load_pass0_rows<0>(r0, tw0);
+        load_pass0_rows<1>(r1, tw0);
     }
     for (int64_t it = 1; gb >= 0; ++it) {
         const int64_t gn = unit_of(units, blockIdx.x, gridDim.x, it);
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kBig.TB) void ols_big_kernel(FusedArgs A) {
         const __amdgpu_buffer_rsrc_t rtw = buf_rsrc(twp, (uint32_t)kBig.twoff[kBig.npass] * 8u);
         const __amdgpu_buffer_rsrc_t rh = buf_rsrc(hp, (uint32_t)kBig.N * 8u);
         big_transform(
-            tb, a, w0, w1, lds, TwBig{rtw, lds_tw, tb}, rh,
+            tb, a, r0, r1, lds, TwBig{rtw, lds_tw, tb}, rh,
             [&](auto Uu, const float2(&v)[64]) {
                 constexpr int u = decltype(Uu)::value;
                 static_for<0, 32>([&](auto J) {
@@ -81,19 +81,19 @@ __global__ __launch_bounds__(kBig.TB) void ols_big_plan_taps_kernel(
         constexpr int r = decltype(Rr)::value;
         a[r] = taps[tb + kBig.TB * pass0_m<kBigGid>(r)];
     });
-    float2 w[15];
-    load_pass0_twiddles<0, 1>(w, twt);
-    fwd_pass0_first<0>(a, w);
+    float2 r[5];
+    load_pass0_rows<0>(r, twt);
+    fwd_pass0_first<0>(a, r);
     put0<0, 0>(tb, a, lds);
-    load_pass0_twiddles<1, 1>(w, twt);
-    fwd_pass0_first<1>(a, w);
+    pass0_twiddles<0, 16, 32, false>(a, r);
+    load_pass0_rows<1>(r, twt);
+    fwd_pass0_first<1>(a, r);
     put0<1, 0>(tb, a, lds);
+    pass0_twiddles<1, 16, 32, false>(a, r);
     constexpr float scale = 1.0f / kBig.N;
     static_for<0, 2>([&](auto Hh) {
         constexpr int h = decltype(Hh)::value;
         if constexpr (h == 1) {
-            pass0_twiddles<0, 16, 32, false>(a, twt);
-            pass0_twiddles<1, 16, 32, false>(a, twt);
             __syncthreads();
             put0<0, 1>(tb, a, lds);
             put0<1, 1>(tb, a, lds);

@@ -109,41 +109,66 @@ __device__ __forceinline__ void inv_vt(float2 (&c)[32], const TW &tw) {
     dft<32, 1>(c);
 }
 
+// Pass-0 twiddles W^(t k) (t = tb + 512 U, k in [1, 32)) of virtual
+// thread U are formed in registers from the five table rows k = 1, 2, 4,
+// 8, 16, which a thread loads once and keeps for all its blocks (they do
+// not depend on the block): with k = 4 i + j, W^(t k) = W^(4 t i) W^(t j),
+// where W^(t j) (j < 4) and W^(4 t i) (i < 8) are rows or products of
+// two or three rows.  Each value carries at most five table roundings and
+// four products.
+template <int U, class TW>
+__device__ __forceinline__ void load_pass0_rows(float2 (&r)[5], const TW &tw) {
+    static_for<0, 5>([&](auto Bb) {
+        r[decltype(Bb)::value] = tw(ic<0>{}, ic<U>{}, ic<(1 << decltype(Bb)::value)>{});
+    });
+}
+// The rows are requested again where they are needed after a phase that
+// holds many registers (the empty asm makes the request a new one, so the
+// compiler does not keep the earlier values live across that phase).
+template <class TW>
+__device__ __forceinline__ void reload_pass0_rows(float2 (&r0)[5], float2 (&r1)[5], const TW &tw) {
+    TW t = tw;
+    asm volatile("" : "+v"(t.tb));
+    load_pass0_rows<0>(r0, t);
+    load_pass0_rows<1>(r1, t);
+}
 // Pass 0 of virtual thread U is split by its output index k: the DFT and
 // the twiddles of k < 16 (the first half's outputs) come first, the
 // twiddles of k >= 16 only when the second half goes to LDS.  In the
 // inverse all conjugate twiddles are applied just before the last DFT.
-// pass0_twiddles requests and applies the twiddles of outputs K0 .. K1-1
-// in one go (the taps planner's second-half twiddles).
-template <int U, int K0, int K1, bool CONJ, class TW>
-__device__ __forceinline__ void pass0_twiddles(float2 (&a)[64], const TW &tw) {
+// pass0_twiddles applies the twiddles of outputs K0 .. K1-1.
+template <int U, int K0, int K1, bool CONJ>
+__device__ __forceinline__ void pass0_twiddles(float2 (&a)[64], const float2 (&r)[5]) {
     __builtin_amdgcn_sched_barrier(0);
-    static_for<(K0 > 0 ? K0 : 1), K1>([&](auto Kk) {
-        constexpr int k = decltype(Kk)::value;
-        const float2 w = tw(ic<0>{}, ic<U>{}, Kk);
-        a[32 * U + k] = CONJ ? cmulc(a[32 * U + k], w) : cmul(a[32 * U + k], w);
+    const float2 l3 = cmul(r[0], r[1]);     // W^(3t)
+    static_for<(K0 >> 2), ((K1 - 1) >> 2) + 1>([&](auto Ii) {
+        constexpr int i = decltype(Ii)::value;
+        float2 hi = r[0];                   // W^(4 t i), i > 0
+        if constexpr (i == 1) hi = r[2];
+        if constexpr (i == 2) hi = r[3];
+        if constexpr (i == 3) hi = cmul(r[2], r[3]);
+        if constexpr (i == 4) hi = r[4];
+        if constexpr (i == 5) hi = cmul(r[4], r[2]);
+        if constexpr (i == 6) hi = cmul(r[4], r[3]);
+        if constexpr (i == 7) hi = cmul(r[4], cmul(r[2], r[3]));
+        static_for<0, 4>([&](auto Jj) {
+            constexpr int j = decltype(Jj)::value;
+            constexpr int k = 4 * i + j;
+            if constexpr (k >= K0 && k < K1 && k > 0) {
+                const float2 lo = j == 1 ? r[0] : j == 2 ? r[1] : l3;
+                const float2 w = i == 0 ? lo : j == 0 ? hi : cmul(hi, lo);
+                a[32 * U + k] = CONJ ? cmulc(a[32 * U + k], w) : cmul(a[32 * U + k], w);
+            }
+        });
     });
     __builtin_amdgcn_sched_barrier(0);
 }
-// Forward pass 0 of virtual thread U with its twiddles of k < 16 already
-// in registers (requested before the previous block's stores: memory
-// operations complete in order, stores included, so a load issued after a
-// burst of stores would wait for the burst).
+// Forward pass 0 of virtual thread U with the twiddles of k < 16.
 template <int U>
-__device__ __forceinline__ void fwd_pass0_first(float2 (&a)[64], const float2 (&w)[15]) {
+__device__ __forceinline__ void fwd_pass0_first(float2 (&a)[64], const float2 (&r)[5]) {
     __builtin_amdgcn_sched_barrier(0);
     dft_at<32, -1, 32 * U>(a);
-    static_for<1, 16>([&](auto Kk) {
-        constexpr int k = decltype(Kk)::value;
-        a[32 * U + k] = cmul(a[32 * U + k], w[k - 1]);
-    });
-    __builtin_amdgcn_sched_barrier(0);
-}
-template <int U, int K0, int N, class TW>
-__device__ __forceinline__ void load_pass0_twiddles(float2 (&w)[N], const TW &tw) {
-    static_for<0, N>([&](auto Ii) {
-        w[decltype(Ii)::value] = tw(ic<0>{}, ic<U>{}, ic<K0 + decltype(Ii)::value>{});
-    });
+    pass0_twiddles<U, 1, 16, false>(a, r);
 }
 
 // Passes 1 and 2 (forward), the product with H and inverse passes 2 and 1
@@ -190,70 +215,45 @@ __device__ __forceinline__ void big_half(int tb, float2 *lds, const TW &tw,
 }
 
 // Step 4 of one block, ending in the store: a holds the gathered block in
-// the pass-0 layout and w0, w1 the forward pass-0 twiddles of k < 16 of
-// both virtual threads; out(ic<U>, a) stores virtual thread U's 32 results
+// the pass-0 layout and r0, r1 the pass-0 twiddle rows of both virtual
+// threads (requested again at the end of each half, and left loaded for
+// the next block); out(ic<U>, a) stores virtual thread U's 32 results
 // (registers 32 U .. 32 U + 31 of a, pass-0 layout) once they are final,
 // and next(ic<U>, a) may then refill those registers (the next block's
-// input, requested while this block finishes).  w0, w1 are reloaded for
-// the next block before the last stores.
+// input, requested while this block finishes).
 template <class TW, class OUT, class NEXT>
-__device__ __forceinline__ void big_transform(int tb, float2 (&a)[64], float2 (&w0)[15],
-                                              float2 (&w1)[15], float2 *lds, const TW &tw,
+__device__ __forceinline__ void big_transform(int tb, float2 (&a)[64], float2 (&r0)[5],
+                                              float2 (&r1)[5], float2 *lds, const TW &tw,
                                               __amdgpu_buffer_rsrc_t Hp, const OUT &out,
                                               const NEXT &next) {
     // forward pass 0; the first half's outputs go to LDS as soon as a
     // virtual thread is done
-    fwd_pass0_first<0>(a, w0);
+    fwd_pass0_first<0>(a, r0);
     __syncthreads();                 // the previous block's LDS accesses are done
     put0<0, 0>(tb, a, lds);
-    fwd_pass0_first<1>(a, w1);
+    fwd_pass0_first<1>(a, r1);
     put0<1, 0>(tb, a, lds);
     __syncthreads();
-    // the second half's forward twiddles are requested at the end of the
-    // first half, the conjugate twiddles of virtual thread 0 at the end of
-    // the second; the first half's results wait untwiddled in registers
-    // k < 16 until the last DFT
-    float2 wf0[16], wf1[16];
-    big_half<0>(tb, lds, tw, Hp, [&] {
-        load_pass0_twiddles<0, 16>(wf0, tw);
-        load_pass0_twiddles<1, 16>(wf1, tw);
-    });
+    // the first half's results wait untwiddled in registers k < 16 until
+    // the last DFT
+    big_half<0>(tb, lds, tw, Hp, [&] { reload_pass0_rows(r0, r1, tw); });
     get0<0, 0>(tb, a, lds);
     get0<1, 0>(tb, a, lds);
-    static_for<16, 32>([&](auto Kk) {
-        constexpr int k = decltype(Kk)::value;
-        a[k] = cmul(a[k], wf0[k - 16]);
-        a[32 + k] = cmul(a[32 + k], wf1[k - 16]);
-    });
+    pass0_twiddles<0, 16, 32, false>(a, r0);
+    pass0_twiddles<1, 16, 32, false>(a, r1);
     __syncthreads();
     put0<0, 1>(tb, a, lds);
     put0<1, 1>(tb, a, lds);
     __syncthreads();
-    float2 wc[31];
-    big_half<1>(tb, lds, tw, Hp, [&] { load_pass0_twiddles<0, 1>(wc, tw); });
+    big_half<1>(tb, lds, tw, Hp, [&] { reload_pass0_rows(r0, r1, tw); });
     get0<0, 1>(tb, a, lds);
-    static_for<1, 32>([&](auto Kk) {
-        constexpr int k = decltype(Kk)::value;
-        a[k] = cmulc(a[k], wc[k - 1]);
-    });
+    pass0_twiddles<0, 1, 32, true>(a, r0);
     dft_at<32, 1, 0>(a);
-    // virtual thread 1's twiddles come before the stores and the next
-    // block's input
-    __builtin_amdgcn_sched_barrier(0);
-    load_pass0_twiddles<1, 1>(wc, tw);
-    __builtin_amdgcn_sched_barrier(0);
     out(ic<0>{}, a);
     next(ic<0>{}, a);
     get0<1, 1>(tb, a, lds);
-    static_for<1, 32>([&](auto Kk) {
-        constexpr int k = decltype(Kk)::value;
-        a[32 + k] = cmulc(a[32 + k], wc[k - 1]);
-    });
+    pass0_twiddles<1, 1, 32, true>(a, r1);
     dft_at<32, 1, 32>(a);
-    __builtin_amdgcn_sched_barrier(0);
-    load_pass0_twiddles<0, 1>(w0, tw);
-    load_pass0_twiddles<1, 1>(w1, tw);
-    __builtin_amdgcn_sched_barrier(0);
     out(ic<1>{}, a);
     next(ic<1>{}, a);
 }

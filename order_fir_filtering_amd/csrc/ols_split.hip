@@ -124,6 +124,13 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
     const __amdgpu_buffer_rsrc_t rc0 = buf_rsrc(slot + kNs, (uint32_t)kNs * 8u);
     const int Mm1 = A.M - 1;
     const int64_t units = A.nblk * A.nchan;
+    // pass-0 twiddle rows of both virtual threads, the same for every block
+    float2 r0[5], r1[5];
+    {
+        const TwBig tw0{buf_rsrc(A.tw, (uint32_t)kBig.twoff[kBig.npass] * 8u), lds_tw, tb};
+        load_pass0_rows<0>(r0, tw0);
+        load_pass0_rows<1>(r1, tw0);
+    }
     for (int64_t it = 0;; ++it) {
         const int64_t gb = unit_of(units, blockIdx.x, gridDim.x, it);
         if (gb < 0) break;
@@ -141,7 +148,7 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
         const __amdgpu_buffer_rsrc_t rtt1 = buf_rsrc(ttp + kNs, (uint32_t)kNs * 8u);
         const TwBig tw{rtw, lds_tw, tb};
 
-        float2 a[64], w0[15], w1[15];
+        float2 a[64];
         if (g0 >= 0 && g0 + kRT * kNs <= A.nsamples) {
             const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc + g0, (uint32_t)(kRT * kNs) * 8u);
             split_gather(a, tb, [&](int j, int off) {
@@ -165,13 +172,10 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
                 return make_float2(u.x + v.x, u.y + v.y);
             }, rtt1, ra1);
         }
-        // (requested after the gather: pass 0 needs all of it first anyway)
-        load_pass0_twiddles<0, 1>(w0, tw);
-        load_pass0_twiddles<1, 1>(w1, tw);
 
         // first half-spectrum: c_0 to the slot, a_1 back from it
         big_transform(
-            tb, a, w0, w1, lds, tw, rh0,
+            tb, a, r0, r1, lds, tw, rh0,
             [&](auto Uu, const float2(&v)[64]) {
                 constexpr int u = decltype(Uu)::value;
                 static_for<0, 32>([&](auto J) {
@@ -196,7 +200,7 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
             buf_rsrc(A.y + c * A.stride + i * A.L, (uint32_t)yn * 8u);
         const int qo = tb - Mm1;
         big_transform(
-            tb, a, w0, w1, lds, tw, rh1,
+            tb, a, r0, r1, lds, tw, rh1,
             [&](auto Uu, const float2(&v)[64]) {
                 split_combine<decltype(Uu)::value>(v, tb, qo, rc0, rtt1, ry);
             },
