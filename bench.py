@@ -47,6 +47,11 @@ def parse():
                     help="untimed warm-up steps (default: about one second of steps)")
     ap.add_argument("--workload", default="cfg2",
                     help="cfg1..cfg5 (default cfg2: M=1025, N=4096, 4 calls)")
+    ap.add_argument("--host-stream", action="store_true",
+                    help="also time the host-resident streaming call (pinned host input "
+                         "and output, copies overlapped with filtering); adds host_stream")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="samples per channel per step of the host-resident call (0: default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -302,6 +307,68 @@ def measured_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
+def host_stream(args, inp, fo, torch, stream):
+    """End-to-end rate of the host-resident streaming call on the same
+    workload: input in pinned host memory, output back to pinned host memory,
+    host-to-device copy, filtering and device-to-host copy pipelined by the
+    library.  The host link bounds it; the plain pinned copy rates of the
+    same bytes are reported beside it."""
+    w = inp.workload
+    sptr = stream.cuda_stream
+    xh = torch.from_numpy(inp.x).pin_memory()
+    yh = torch.empty(xh.shape, dtype=xh.dtype, pin_memory=True)
+    plan = fo.Plan(w.M, w.N, w.nchan)
+    if inp.H is not None:
+        plan.set_freq_response(inp.H)
+    else:
+        plan.set_taps(inp.taps)
+    plan.set_state(torch.from_numpy(inp.s0).to("cuda:0"))
+
+    def hstep():
+        pos = 0
+        for c in w.calls:
+            fo.fir_ols_execute_host(plan.handle, xh.data_ptr() + 8 * pos, yh.data_ptr() + 8 * pos,
+                                    c, w.samples, args.chunk, sptr)
+            pos += c
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        hstep()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    hstep()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    reps = max(3, min(200, int(1000.0 / max(e0.elapsed_time(e1), 1e-3))))
+    e0.record(stream)
+    for _ in range(reps):
+        hstep()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    plan.close()
+    # plain pinned copies of the same bytes, one direction at a time
+    xd = torch.empty(xh.shape, dtype=xh.dtype, device="cuda:0")
+    rates = {}
+    for name, dst, src in (("h2d", xd, xh), ("d2h", yh, xd)):
+        dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(5):
+            dst.copy_(src, non_blocking=True)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rates[name] = 5 * xh.numel() * 8 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    samples = w.nchan * w.samples
+    link = min(rates["h2d"], rates["d2h"]) * 1e9 / 8 / 1e6
+    return {"value": round(samples / (ms * 1e-3) / 1e6, 1), "unit": "Msamples/s",
+            "ms_per_step": round(ms, 4), "steps": reps, "pinned": True,
+            "chunk": args.chunk or "default", "h2d_GBps": round(rates["h2d"], 1),
+            "d2h_GBps": round(rates["d2h"], 1),
+            "link_bound_Msamples": round(link, 1),
+            "note": "includes the host link; never the headline value"}
+
+
 def valu_line(workload: str, kern_ms: float):
     """fp32 VALU throughput of the filtering kernel: counted flops per
     launch (committed counter run of the same sources) over the live
@@ -472,6 +539,7 @@ def main():
     copy_gbps = reps * 2 * fx[0].numel() * 4 / (c0.elapsed_time(c1) * 1e-3) / 1e9
 
     plan.close()
+    host = host_stream(args, inp, fo, torch, stream) if args.host_stream else None
     out = {
         "metric": "filtered output Msamples/s (complex fp32) and % of HBM roof, per (M,N)",
         "value": round(value, 1),
@@ -507,6 +575,7 @@ def main():
         },
         "valu": valu_line(w.key, kern_ms),
         "copy_reference_GBps": round(copy_gbps, 1),
+        "host_stream": host,
         "parity": parity,
         "cpu_baseline": base,
         "wall_s": round(wall, 3),

@@ -132,6 +132,39 @@ int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev,
                     int64_t nsamples, int64_t chan_stride, void *stream);
 
 /*
+ * Host-resident streaming (claim 1, steps 2 and 6: the samples arrive from
+ * host memory in chunks and the filtered chunks go back to it).  Filters
+ * nsamples per channel exactly as fir_ols_execute would, carrying the
+ * state, but reads x from and writes y to host memory:
+ *   x_host, y_host  host complex64 [nchan][chan_stride]; page-locked memory
+ *                   (hipHostMalloc, or torch's pin_memory) lets the copies
+ *                   run asynchronously and overlap the filtering; pageable
+ *                   memory works but the runtime stages those copies.
+ *   chunk           samples per channel per step (0: 2^22 / nchan rounded
+ *                   up to whole blocks of L, about 32 MiB per staging slot),
+ *                   clipped to nsamples.
+ * The call cuts the stream into chunks and runs them through two device
+ * staging slots owned by the plan ([nchan][chunk] complex64 each for input
+ * and output, allocated on first use and grown when a larger chunk is
+ * asked for): host-to-device copies on one internal stream, one
+ * fir_ols_execute per chunk on `stream`, device-to-host copies on another
+ * internal stream.  Everything is enqueued before the call returns; the
+ * copies start after the work queued on `stream` before the call, and
+ * `stream` passes the call only after the last output copy, so the caller
+ * synchronizes `stream` before it reads y_host or reuses x_host.  Because
+ * each chunk is a separate filtering call, the outputs equal those of
+ * fir_ols_execute over the same chunks, bit for bit.  Not for HIP graph
+ * capture (internal streams, first-use allocation).  Errors as
+ * fir_ols_execute (FIR_OLS_ERR_ALIAS when the two host ranges overlap,
+ * FIR_OLS_ERR_OOM when the staging slots cannot be allocated); a failure
+ * after the first chunk was enqueued returns FIR_OLS_ERR_HIP with the
+ * state advanced by the chunks already enqueued.
+ */
+int fir_ols_execute_host(fir_ols_plan_t p, const void *x_host, void *y_host,
+                         int64_t nsamples, int64_t chan_stride, int64_t chunk,
+                         void *stream);
+
+/*
  * Replace the state (claim 1, step 3: S0 is the M-1 samples that preceded
  * the call).
  *   s0_dev  device complex64 [nchan][M-1], time order, or NULL for zeros.

@@ -23,14 +23,14 @@ from .build import LIB as LIBRARY_PATH
 __all__ = [
     "FirOlsError", "Plan", "load_library", "LIBRARY_PATH", "EXPORTED",
     "fir_ols_plan", "fir_ols_set_taps", "fir_ols_set_freq_response",
-    "fir_ols_execute", "fir_ols_set_state", "fir_ols_get_state",
+    "fir_ols_execute", "fir_ols_execute_host", "fir_ols_set_state", "fir_ols_get_state",
     "fir_ols_destroy", "fir_ols_block_length", "fir_ols_status_string",
 ]
 
 # Every symbol include/firols.h declares.
 EXPORTED = (
     "fir_ols_plan", "fir_ols_set_taps", "fir_ols_set_freq_response",
-    "fir_ols_execute", "fir_ols_set_state", "fir_ols_get_state",
+    "fir_ols_execute", "fir_ols_execute_host", "fir_ols_set_state", "fir_ols_get_state",
     "fir_ols_destroy", "fir_ols_block_length", "fir_ols_status_string",
 )
 
@@ -69,6 +69,7 @@ def load_library(path: Optional[str] = None):
         "fir_ols_set_taps": (_int, [_vp, _vp, _i64, _int, _vp]),
         "fir_ols_set_freq_response": (_int, [_vp, _vp, _i64, _vp]),
         "fir_ols_execute": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
+        "fir_ols_execute_host": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
         "fir_ols_set_state": (_int, [_vp, _vp, _vp]),
         "fir_ols_get_state": (_int, [_vp, _vp, _vp]),
         "fir_ols_destroy": (_int, [_vp]),
@@ -143,6 +144,16 @@ def fir_ols_execute(plan: int, x, y, nsamples: int, chan_stride: int, stream=Non
            "fir_ols_execute")
 
 
+def fir_ols_execute_host(plan: int, x, y, nsamples: int, chan_stride: int, chunk: int = 0,
+                         stream=None) -> None:
+    """Enqueue the host-resident streaming call: x, y are host addresses (or
+    CPU tensors) of [nchan][chan_stride] complex64; `stream` passes the call
+    after the last output copy."""
+    lib = load_library()
+    _check(lib.fir_ols_execute_host(plan, _ptr(x), _ptr(y), nsamples, chan_stride, chunk,
+                                    _stream(stream)), "fir_ols_execute_host")
+
+
 def fir_ols_set_state(plan: int, s0=None, stream=None) -> None:
     lib = load_library()
     _check(lib.fir_ols_set_state(plan, _ptr(s0), _stream(stream)), "fir_ols_set_state")
@@ -207,6 +218,30 @@ class Plan:
         elif y.shape != x.shape or y.stride() != x.stride() or y.dtype != x.dtype:
             raise FirOlsError(-1, "execute: y must match x in shape, strides and dtype")
         fir_ols_execute(self.handle, x, y, n, stride, stream)
+        return y
+
+    def execute_host(self, x, y=None, chunk: int = 0, stream=None):
+        """Filter a host (CPU, ideally pinned) complex64 tensor x of shape [n]
+        or [nchan, n] through the host-resident streaming call; returns y
+        (a pinned CPU tensor unless given) once the stream has passed it."""
+        import torch
+        if x.dtype != torch.complex64 or x.is_cuda:
+            raise FirOlsError(-1, "execute_host: x must be a complex64 CPU tensor")
+        if x.dim() == 1:
+            if self.nchan != 1:
+                raise FirOlsError(-1, "execute_host: x must be [nchan, n]")
+            n, stride = x.shape[0], max(x.shape[0], 1)
+        elif x.dim() == 2 and x.shape[0] == self.nchan and (x.shape[1] <= 1 or x.stride(1) == 1):
+            n, stride = x.shape[1], max(x.stride(0), x.shape[1])
+        else:
+            raise FirOlsError(-1, "execute_host: x must be [nchan, n] with unit inner stride")
+        if y is None:
+            y = torch.empty_strided(x.shape, x.stride(), dtype=x.dtype, pin_memory=True)
+        elif y.shape != x.shape or y.stride() != x.stride() or y.dtype != x.dtype or y.is_cuda:
+            raise FirOlsError(-1, "execute_host: y must be a CPU tensor matching x")
+        fir_ols_execute_host(self.handle, x, y, n, stride, chunk, stream)
+        s = stream if stream is not None else torch.cuda.current_stream()
+        (s if hasattr(s, "synchronize") else torch.cuda.current_stream()).synchronize()
         return y
 
     def set_state(self, s0=None, stream=None) -> None:

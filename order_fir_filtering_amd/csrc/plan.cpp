@@ -10,22 +10,7 @@
 #include <vector>
 
 #include "kernels.hpp"
-
-struct fir_ols_plan_s {
-    int device = 0;
-    int logn = 0;
-    int64_t M = 0, N = 0, L = 0, nchan = 0;
-    float2 *H = nullptr;          // N values, kernel order, scaled by 1/N
-    float2 *tw = nullptr;         // twiddle table
-    float2 *taps = nullptr;       // N zero-padded taps, staging for set_taps
-    float2 *state[2] = {nullptr, nullptr};   // [nchan][M-1] each
-    int parity = 0;               // state[parity] is the current state
-    int max_groups = 0;           // resident workgroups of the filtering kernel
-    bool has_filter = false;
-    // split path (N = 65536)
-    float2 *tw_top = nullptr;     // W_N^{q k0}, k0 = 0 .. RT-1
-    float2 *scratch = nullptr;    // max_groups slots of N values
-};
+#include "plan.hpp"
 
 namespace {
 
@@ -44,6 +29,7 @@ bool on_plan_device(const fir_ols_plan_s *p) {
 }
 
 void release(fir_ols_plan_s *p) {
+    release_host_stream(p);
     (void)hipFree(p->tw_top);
     (void)hipFree(p->scratch);
     (void)hipFree(p->H);

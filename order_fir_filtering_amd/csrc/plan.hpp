@@ -1,0 +1,32 @@
+// The plan object behind the C ABI's opaque handle (shared by the
+// library's host sources; not part of the public interface).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+struct fir_ols_plan_s {
+    int device = 0;
+    int logn = 0;
+    int64_t M = 0, N = 0, L = 0, nchan = 0;
+    float2 *H = nullptr;          // N values, kernel order, scaled by 1/N
+    float2 *tw = nullptr;         // twiddle table
+    float2 *taps = nullptr;       // N zero-padded taps, staging for set_taps
+    float2 *state[2] = {nullptr, nullptr};   // [nchan][M-1] each
+    int parity = 0;               // state[parity] is the current state
+    int max_groups = 0;           // resident workgroups of the filtering kernel
+    bool has_filter = false;
+    // split path (N = 65536)
+    float2 *tw_top = nullptr;     // W_N^{q k0}, k0 = 0 .. RT-1
+    float2 *scratch = nullptr;    // max_groups slots of N values
+    // host-resident streaming (fir_ols_execute_host), created on first use
+    int64_t hs_chunk = 0;                      // samples per channel of a staging slot
+    float2 *hs_x[2] = {nullptr, nullptr};      // device input slots [nchan][hs_chunk]
+    float2 *hs_y[2] = {nullptr, nullptr};      // device output slots [nchan][hs_chunk]
+    hipStream_t hs_in = nullptr, hs_out = nullptr;   // copy streams (default priority)
+    hipEvent_t hs_ev[8] = {};                  // in[2], comp[2], out[2], start, end
+};
+
+// Frees the host-streaming resources of a plan (no-op when never used).
+void release_host_stream(fir_ols_plan_s *p);
