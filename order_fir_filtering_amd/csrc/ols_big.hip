@@ -19,10 +19,12 @@ namespace firols {
 // long; started together, all CUs reach their memory phase at the same
 // time and share the HBM bandwidth, while a CU alone could move its data
 // about twice as fast.  So when every workgroup has several blocks to do,
-// every second workgroup of each XCD starts about 40% of a block period
-// late, and the two groups' memory phases interleave from then on
-// (measured at M = 8193: 302 -> 289 us per call).
-constexpr uint64_t kStaggerTicks = 1600;   // 16 us of the 100 MHz constant clock
+// the workgroups of each XCD start in three groups, 10 us apart (about a
+// quarter of a block period), and the groups' memory phases interleave
+// from then on (measured at M = 8193: 302 us per call without, 289 with
+// two groups 16 us apart, 281 with three groups 10 us apart).
+constexpr int kStaggerGroups = 3;
+constexpr uint64_t kStaggerTicks = 1000;   // 10 us of the 100 MHz constant clock
 constexpr int kStaggerMinBlocks = 3;       // blocks per workgroup for the stagger to pay
 
 __global__ __launch_bounds__(kBig.TB) void ols_big_kernel(FusedArgs A) {
@@ -32,10 +34,11 @@ __global__ __launch_bounds__(kBig.TB) void ols_big_kernel(FusedArgs A) {
     for (int e = tb; e < kTw1; e += kBig.TB) lds_tw[e] = A.tw[kBig.twoff[1] + e];
     // (the first barrier of the transform orders these writes before use)
     const int64_t units = A.nblk * A.nchan;
-    if ((gridDim.x & 7) == 0 && units >= (int64_t)kStaggerMinBlocks * gridDim.x &&
-        ((blockIdx.x >> 3) & 1)) {
+    if ((gridDim.x & 7) == 0 && units >= (int64_t)kStaggerMinBlocks * gridDim.x) {
+        // (blockIdx.x >> 3 numbers the workgroups within one XCD)
+        const uint64_t wait = (uint64_t)((blockIdx.x >> 3) % kStaggerGroups) * kStaggerTicks;
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        while (__builtin_amdgcn_s_memrealtime() - t0 < kStaggerTicks) __builtin_amdgcn_s_sleep(8);
+        while (__builtin_amdgcn_s_memrealtime() - t0 < wait) __builtin_amdgcn_s_sleep(8);
     }
     // software-pipelined over blocks: the input of the next block is
     // requested as soon as the registers of a virtual thread are free
