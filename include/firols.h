@@ -187,6 +187,17 @@ int fir_ols_get_state(fir_ols_plan_t p, void *s0_out_dev, void *stream);
  */
 int fir_ols_destroy(fir_ols_plan_t p);
 
+/*
+ * Planner choice of N (claim 1, step 1 leaves the FFT length free): the
+ * power of two N >= max(M, 256) that maximizes the predicted output rate
+ * (N - M + 1) x blocks_per_second(N), from a table of block rates measured
+ * on MI355X (one long single-channel call per N).  given_h != 0 allows
+ * N = 65536, which takes its filter only through fir_ols_set_freq_response.
+ * Returns N, FIR_OLS_ERR_INVALID_ARG for M < 1, or FIR_OLS_ERR_UNSUPPORTED
+ * when no allowed N >= M exists.  Pure host arithmetic: no device call.
+ */
+int64_t fir_ols_choose_n(int64_t M, int given_h);
+
 /* Block length L = N - M + 1 of a plan, or a negative status. */
 int64_t fir_ols_block_length(fir_ols_plan_t p);
 

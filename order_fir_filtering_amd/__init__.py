@@ -24,14 +24,14 @@ __all__ = [
     "FirOlsError", "Plan", "load_library", "LIBRARY_PATH", "EXPORTED",
     "fir_ols_plan", "fir_ols_set_taps", "fir_ols_set_freq_response",
     "fir_ols_execute", "fir_ols_execute_host", "fir_ols_set_state", "fir_ols_get_state",
-    "fir_ols_destroy", "fir_ols_block_length", "fir_ols_status_string",
+    "fir_ols_destroy", "fir_ols_block_length", "fir_ols_choose_n", "fir_ols_status_string",
 ]
 
 # Every symbol include/firols.h declares.
 EXPORTED = (
     "fir_ols_plan", "fir_ols_set_taps", "fir_ols_set_freq_response",
     "fir_ols_execute", "fir_ols_execute_host", "fir_ols_set_state", "fir_ols_get_state",
-    "fir_ols_destroy", "fir_ols_block_length", "fir_ols_status_string",
+    "fir_ols_destroy", "fir_ols_block_length", "fir_ols_choose_n", "fir_ols_status_string",
 )
 
 STATUS = {
@@ -74,6 +74,7 @@ def load_library(path: Optional[str] = None):
         "fir_ols_get_state": (_int, [_vp, _vp, _vp]),
         "fir_ols_destroy": (_int, [_vp]),
         "fir_ols_block_length": (_i64, [_vp]),
+        "fir_ols_choose_n": (_i64, [_i64, _int]),
         "fir_ols_status_string": (ctypes.c_char_p, [_int]),
     }
     for name, (res, args) in sig.items():
@@ -175,6 +176,14 @@ def fir_ols_block_length(plan: int) -> int:
     if L < 0:
         raise FirOlsError(int(L), "fir_ols_block_length")
     return int(L)
+
+
+def fir_ols_choose_n(M: int, given_h: bool = False) -> int:
+    """Planner choice of the FFT length N for M taps (see include/firols.h)."""
+    N = load_library().fir_ols_choose_n(M, int(bool(given_h)))
+    if N < 0:
+        raise FirOlsError(int(N), "fir_ols_choose_n")
+    return int(N)
 
 
 def fir_ols_status_string(status: int) -> str:

@@ -252,6 +252,29 @@ int fir_ols_destroy(fir_ols_plan_t p) {
     return e == hipSuccess ? FIR_OLS_OK : FIR_OLS_ERR_HIP;
 }
 
+int64_t fir_ols_choose_n(int64_t M, int given_h) {
+    // blocks per second of N = 2^8 .. 2^16 on MI355X, measured by
+    // order_fir_filtering_amd/tune_n.py (one call of many blocks per N)
+    static const double kBlocksPerSecond[] = {
+        1440727324.0, 695416587.3, 361791268.1,
+        161137501.6, 69294385.8, 15297903.4,
+        7940777.2, 6837285.2, 2221459.8};
+    if (M < 1) return FIR_OLS_ERR_INVALID_ARG;
+    const int max_logn = given_h ? 16 : 15;
+    int64_t best = FIR_OLS_ERR_UNSUPPORTED;
+    double best_rate = 0.0;
+    for (int logn = 8; logn <= max_logn; ++logn) {
+        const int64_t N = (int64_t)1 << logn;
+        if (N < M) continue;
+        const double rate = (double)(N - M + 1) * kBlocksPerSecond[logn - 8];
+        if (rate > best_rate) {
+            best_rate = rate;
+            best = N;
+        }
+    }
+    return best;
+}
+
 int64_t fir_ols_block_length(fir_ols_plan_t p) {
     return p ? p->L : (int64_t)FIR_OLS_ERR_INVALID_ARG;
 }

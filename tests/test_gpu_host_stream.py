@@ -1,4 +1,4 @@
-"""fir_ols_execute_host: host-resident streaming through the C ABI.
+"""fir_ols_execute_host (host-resident streaming) and fir_ols_choose_n through the C ABI.
 
 The host call cuts the stream into chunks and runs one filtering call per
 chunk, so its output must equal, bit for bit, fir_ols_execute over the same
@@ -137,3 +137,21 @@ def test_host_stream_argument_checks():
                                     None)
         assert e.value.status == -1                 # stride below nsamples
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M", [1, 203, 1025, 5000])
+def test_planner_choice_runs_and_matches_the_oracle(M):
+    """A plan with the N that fir_ols_choose_n picks filters correctly."""
+    N = fo.fir_ols_choose_n(M)
+    say(f"planner: M={M} -> N={N}")
+    rng = np.random.default_rng(M)
+    h = W.complex_taps(rng, M).astype(np.complex64)
+    x = W.complex_normal(rng, (1, 3 * N + 17))
+    s0 = W.complex_normal(rng, (1, M - 1))
+    from gpu_util import run_calls
+    with fo.Plan(M, N, 1) as p:
+        p.set_taps(h)
+        y = run_calls(p, x, [x.shape[1]], s0)
+    idx = np.arange(0, x.shape[1], 7)
+    ref = oracle.fir_direct_multi(h, x, s0, idx=idx, threads=THREADS)
+    check(y[:, idx], ref, h, x, s0, f"planner M={M} N={N}")

@@ -1,0 +1,44 @@
+"""fir_ols_choose_n (host arithmetic only: runs without a GPU).
+
+The library's table of block rates must be the one the committed sweep
+(order_fir_filtering_amd/tune_n.py) wrote to profiles/n_sweep.json, and the
+choice must maximize (N - M + 1) x blocks_per_second(N) over the allowed N.
+"""
+import json
+import os
+
+import pytest
+
+import order_fir_filtering_amd as fo
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SWEEP = {int(k): v for k, v in json.load(open(os.path.join(ROOT, "profiles", "n_sweep.json"))).items()}
+
+
+def best(M, given_h):
+    cands = [N for N in SWEEP if N >= M and (given_h or N <= 32768)]
+    return max(cands, key=lambda N: (N - M + 1) * SWEEP[N]) if cands else None
+
+
+@pytest.mark.parametrize("given_h", [False, True])
+def test_choice_maximizes_the_measured_rate(given_h):
+    for M in list(range(1, 300)) + [511, 512, 513, 1025, 2049, 4097, 8193, 16384, 16385,
+                                    32768, 40000, 65536]:
+        want = best(M, given_h)
+        if want is None:
+            with pytest.raises(fo.FirOlsError) as e:
+                fo.fir_ols_choose_n(M, given_h)
+            assert e.value.status == -2
+            continue
+        N = fo.fir_ols_choose_n(M, given_h)
+        assert N == want, (M, N, want)
+        assert N >= max(M, 256) and N & (N - 1) == 0
+
+
+def test_choice_arguments():
+    with pytest.raises(fo.FirOlsError) as e:
+        fo.fir_ols_choose_n(0)
+    assert e.value.status == -1
+    assert fo.fir_ols_choose_n(65536, True) == 65536
+    with pytest.raises(fo.FirOlsError):
+        fo.fir_ols_choose_n(65537, True)
