@@ -29,6 +29,13 @@ struct FusedCfg {
     // block (128 VGPRs) its extra offsets would spill, so that size keeps
     // pointer I/O.
     static constexpr bool WAVE_IO = G.TB >= 64 && G.TB < 1024;
+    // At N = 8192 one block takes 66 KB of LDS and 8 waves, so two
+    // workgroups fit a CU if a thread keeps to 128 VGPRs (4 waves per SIMD):
+    // the second workgroup's gather and store then overlap the first one's
+    // transform.  Measured with one long call at M = 2049: 94 GS/s with one
+    // workgroup per CU (158 VGPRs), 131 GS/s with two (128 VGPRs, some
+    // spilled to scratch).  N = 16384 (132 KB of LDS) fits only one.
+    static constexpr int MIN_WAVES_PER_SIMD = G.logn == 13 ? 4 : 1;
 };
 
 // One block: gather (step 3), FFT / product / inverse FFT (step 4), store
@@ -101,7 +108,8 @@ __device__ __forceinline__ void process_block_wave(const FusedArgs &A, int64_t g
 }
 
 template <int GID>
-__global__ __launch_bounds__(FusedCfg<GID>::WG) void ols_fused_kernel(FusedArgs A) {
+__global__ __launch_bounds__(FusedCfg<GID>::WG, FusedCfg<GID>::MIN_WAVES_PER_SIMD) void ols_fused_kernel(
+    FusedArgs A) {
     using C = FusedCfg<GID>;
     constexpr Geo G = make_geo(GID);
     __shared__ float2 lds[C::LDSN];

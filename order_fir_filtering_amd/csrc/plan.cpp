@@ -256,9 +256,9 @@ int64_t fir_ols_choose_n(int64_t M, int given_h) {
     // blocks per second of N = 2^8 .. 2^16 on MI355X, measured by
     // order_fir_filtering_amd/tune_n.py (one call of many blocks per N)
     static const double kBlocksPerSecond[] = {
-        1440727324.0, 695416587.3, 361791268.1,
-        161137501.6, 69294385.8, 15297903.4,
-        7940777.2, 6837285.2, 2221459.8};
+        1409070468.0, 695496558.7, 359583480.4,
+        159442253.4, 69565365.6, 21163666.1,
+        7907989.3, 6760967.2, 2208279.9};
     if (M < 1) return FIR_OLS_ERR_INVALID_ARG;
     const int max_logn = given_h ? 16 : 15;
     int64_t best = FIR_OLS_ERR_UNSUPPORTED;
