@@ -75,16 +75,15 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan);
 
 /*
  * Set the filter from its taps (claim 1, step 1, first case): the taps are
- * zero-padded to N and transformed on the GPU; H is kept scaled by 1/N so
- * the inverse transform of step 4 needs no separate scaling.
+ * zero-padded to N and transformed, on the GPU for N <= 32768 and on the
+ * host in float64 for N = 65536; H is kept scaled by 1/N so the inverse
+ * transform of step 4 needs no separate scaling.
  *   h_host      host array: M float32 taps (is_complex == 0) or M
  *               interleaved complex64 taps (is_complex != 0); copied
  *               before return, the caller keeps ownership.
  *   M           must equal the plan's M.
  *   stream      stream the work is ordered on (after earlier executes).
  * Returns after H is in place.  Leaves the state unchanged.
- * FIR_OLS_ERR_UNSUPPORTED for N = 65536 (that size takes its filter through
- * fir_ols_set_freq_response).
  */
 int fir_ols_set_taps(fir_ols_plan_t p, const float *h_host, int64_t M,
                      int is_complex, void *stream);
@@ -191,12 +190,11 @@ int fir_ols_destroy(fir_ols_plan_t p);
  * Planner choice of N (claim 1, step 1 leaves the FFT length free): the
  * power of two N >= max(M, 256) that maximizes the predicted output rate
  * (N - M + 1) x blocks_per_second(N), from a table of block rates measured
- * on MI355X (one long single-channel call per N).  given_h != 0 allows
- * N = 65536, which takes its filter only through fir_ols_set_freq_response.
- * Returns N, FIR_OLS_ERR_INVALID_ARG for M < 1, or FIR_OLS_ERR_UNSUPPORTED
- * when no allowed N >= M exists.  Pure host arithmetic: no device call.
+ * on MI355X (one long single-channel call per N).  Returns N,
+ * FIR_OLS_ERR_INVALID_ARG for M < 1, or FIR_OLS_ERR_UNSUPPORTED for
+ * M > 65536.  Pure host arithmetic: no device call.
  */
-int64_t fir_ols_choose_n(int64_t M, int given_h);
+int64_t fir_ols_choose_n(int64_t M);
 
 /* Block length L = N - M + 1 of a plan, or a negative status. */
 int64_t fir_ols_block_length(fir_ols_plan_t p);

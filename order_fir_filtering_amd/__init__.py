@@ -74,7 +74,7 @@ def load_library(path: Optional[str] = None):
         "fir_ols_get_state": (_int, [_vp, _vp, _vp]),
         "fir_ols_destroy": (_int, [_vp]),
         "fir_ols_block_length": (_i64, [_vp]),
-        "fir_ols_choose_n": (_i64, [_i64, _int]),
+        "fir_ols_choose_n": (_i64, [_i64]),
         "fir_ols_status_string": (ctypes.c_char_p, [_int]),
     }
     for name, (res, args) in sig.items():
@@ -178,9 +178,9 @@ def fir_ols_block_length(plan: int) -> int:
     return int(L)
 
 
-def fir_ols_choose_n(M: int, given_h: bool = False) -> int:
+def fir_ols_choose_n(M: int) -> int:
     """Planner choice of the FFT length N for M taps (see include/firols.h)."""
-    N = load_library().fir_ols_choose_n(M, int(bool(given_h)))
+    N = load_library().fir_ols_choose_n(M)
     if N < 0:
         raise FirOlsError(int(N), "fir_ols_choose_n")
     return int(N)

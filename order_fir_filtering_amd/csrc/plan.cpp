@@ -5,8 +5,11 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+#include <complex>
 #include <cstdint>
 #include <new>
+#include <utility>
 #include <vector>
 
 #include "kernels.hpp"
@@ -48,6 +51,33 @@ bool is_big(const fir_ols_plan_s *p) { return p->logn == firols::kBigLogN; }
 int table_geometry(const fir_ols_plan_s *p) {
     return is_big(p) ? firols::big_geometry() : firols::fused_geometry(p->logn);
 }
+
+// In-place radix-2 DFT X[q] = sum_m x[m] e^{-2 pi i q m / N} in float64 (the
+// split path's frequency response, claim 1 step 1: the N-point FFT of the
+// zero-padded taps).  Iterative Cooley-Tukey: bit-reversal permutation, then
+// log2 N butterfly stages with twiddles from std::polar per stage.
+void host_fft(std::vector<std::complex<double>> &a) {
+    const size_t n = a.size();
+    for (size_t i = 1, j = 0; i < n; ++i) {
+        size_t bit = n >> 1;
+        for (; j & bit; bit >>= 1) j ^= bit;
+        j ^= bit;
+        if (i < j) std::swap(a[i], a[j]);
+    }
+    for (size_t len = 2; len <= n; len <<= 1) {
+        const size_t half = len >> 1;
+        std::vector<std::complex<double>> w(half);
+        for (size_t k = 0; k < half; ++k) w[k] = std::polar(1.0, -2.0 * M_PI * (double)k / (double)len);
+        for (size_t i = 0; i < n; i += len)
+            for (size_t k = 0; k < half; ++k) {
+                const std::complex<double> u = a[i + k], v = a[i + k + half] * w[k];
+                a[i + k] = u + v;
+                a[i + k + half] = u - v;
+            }
+    }
+}
+
+int upload_freq_response(fir_ols_plan_t p, const float *H_host, hipStream_t s);
 
 }  // namespace
 
@@ -119,14 +149,26 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
     return FIR_OLS_OK;
 }
 
+
 int fir_ols_set_taps(fir_ols_plan_t p, const float *h_host, int64_t M, int is_complex,
                      void *stream) {
     if (!p || !h_host || M != p->M) return FIR_OLS_ERR_INVALID_ARG;
-    // The taps transform of the split path (N = 65536) is switched off: an
-    // earlier version of it ended in a GPU memory fault whose cause is not
-    // found yet.  fir_ols_set_freq_response covers that size.
-    if (is_split(p)) return FIR_OLS_ERR_UNSUPPORTED;
     if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
+    if (is_split(p)) {
+        // N = 65536: H is computed on the host (float64) and takes the
+        // frequency-response path; no planning kernel runs for this size
+        std::vector<std::complex<double>> a((size_t)p->N, 0.0);
+        for (int64_t m = 0; m < M; ++m)
+            a[m] = is_complex ? std::complex<double>(h_host[2 * m], h_host[2 * m + 1])
+                              : std::complex<double>(h_host[m], 0.0);
+        host_fft(a);
+        std::vector<float> H((size_t)(2 * p->N));
+        for (int64_t q = 0; q < p->N; ++q) {
+            H[2 * q] = (float)a[q].real();
+            H[2 * q + 1] = (float)a[q].imag();
+        }
+        return upload_freq_response(p, H.data(), (hipStream_t)stream);
+    }
     std::vector<float2> padded((size_t)p->N, make_float2(0.f, 0.f));
     for (int64_t m = 0; m < M; ++m)
         padded[m] = is_complex ? make_float2(h_host[2 * m], h_host[2 * m + 1])
@@ -146,6 +188,17 @@ int fir_ols_set_taps(fir_ols_plan_t p, const float *h_host, int64_t M, int is_co
 int fir_ols_set_freq_response(fir_ols_plan_t p, const float *H_host, int64_t N, void *stream) {
     if (!p || !H_host || N != p->N) return FIR_OLS_ERR_INVALID_ARG;
     if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
+    return upload_freq_response(p, H_host, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// H (unscaled, natural bin order, interleaved complex) scaled by 1/N into
+// the kernels' order on the device.
+int upload_freq_response(fir_ols_plan_t p, const float *H_host, hipStream_t s) {
+    const int64_t N = p->N;
     std::vector<int64_t> perm((size_t)N);
     if (is_split(p))
         firols::build_split_h_permutation(p->logn, perm.data());
@@ -157,13 +210,16 @@ int fir_ols_set_freq_response(fir_ols_plan_t p, const float *H_host, int64_t N, 
         const int64_t b = perm[i];
         Hk[i] = make_float2(H_host[2 * b] * scale, H_host[2 * b + 1] * scale);
     }
-    hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipMemcpyAsync(p->H, Hk.data(), N * sizeof(float2), hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return FIR_OLS_ERR_HIP;
     p->has_filter = true;
     return FIR_OLS_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev, int64_t nsamples,
                     int64_t chan_stride, void *stream) {
@@ -252,7 +308,7 @@ int fir_ols_destroy(fir_ols_plan_t p) {
     return e == hipSuccess ? FIR_OLS_OK : FIR_OLS_ERR_HIP;
 }
 
-int64_t fir_ols_choose_n(int64_t M, int given_h) {
+int64_t fir_ols_choose_n(int64_t M) {
     // blocks per second of N = 2^8 .. 2^16 on MI355X, measured by
     // order_fir_filtering_amd/tune_n.py (one call of many blocks per N)
     static const double kBlocksPerSecond[] = {
@@ -260,10 +316,9 @@ int64_t fir_ols_choose_n(int64_t M, int given_h) {
         159442253.4, 69565365.6, 21163666.1,
         7907989.3, 6760967.2, 2208279.9};
     if (M < 1) return FIR_OLS_ERR_INVALID_ARG;
-    const int max_logn = given_h ? 16 : 15;
     int64_t best = FIR_OLS_ERR_UNSUPPORTED;
     double best_rate = 0.0;
-    for (int logn = 8; logn <= max_logn; ++logn) {
+    for (int logn = 8; logn <= 16; ++logn) {
         const int64_t N = (int64_t)1 << logn;
         if (N < M) continue;
         const double rate = (double)(N - M + 1) * kBlocksPerSecond[logn - 8];

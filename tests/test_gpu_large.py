@@ -17,12 +17,6 @@ import workloads as W
 from gpu_util import check, run_calls, say, to_dev
 
 pytestmark = pytest.mark.gpu
-# The first run of an earlier N = 65536 taps transform (fir_ols_set_taps)
-# faulted the GPU with no cause found on the CPU; that entry point is
-# switched off for N = 65536 and its one case stays skipped until the cause
-# is found.
-SKIP_TAPS_65536 = pytest.mark.skip(
-    reason="set_taps at N=65536 is switched off after an unexplained GPU fault")
 THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
@@ -108,7 +102,7 @@ def test_large_sizes(N, M, n, nchan, seed):
         np.testing.assert_array_equal(st[c], oracle.state_next(x[c], s0[c], M))
 
 
-@pytest.mark.parametrize("N,M", [(32768, 8193), pytest.param(65536, 16385, marks=SKIP_TAPS_65536)])
+@pytest.mark.parametrize("N,M", [(32768, 8193), (65536, 16385)])
 def test_large_taps_and_freq_response_agree_and_stream(N, M):
     say(f"large taps vs H, chunked calls: N={N} M={M}")
     rng = np.random.default_rng(N + M)

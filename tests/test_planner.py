@@ -15,22 +15,21 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SWEEP = {int(k): v for k, v in json.load(open(os.path.join(ROOT, "profiles", "n_sweep.json"))).items()}
 
 
-def best(M, given_h):
-    cands = [N for N in SWEEP if N >= M and (given_h or N <= 32768)]
+def best(M):
+    cands = [N for N in SWEEP if N >= M]
     return max(cands, key=lambda N: (N - M + 1) * SWEEP[N]) if cands else None
 
 
-@pytest.mark.parametrize("given_h", [False, True])
-def test_choice_maximizes_the_measured_rate(given_h):
+def test_choice_maximizes_the_measured_rate():
     for M in list(range(1, 300)) + [511, 512, 513, 1025, 2049, 4097, 8193, 16384, 16385,
                                     32768, 40000, 65536]:
-        want = best(M, given_h)
+        want = best(M)
         if want is None:
             with pytest.raises(fo.FirOlsError) as e:
-                fo.fir_ols_choose_n(M, given_h)
+                fo.fir_ols_choose_n(M)
             assert e.value.status == -2
             continue
-        N = fo.fir_ols_choose_n(M, given_h)
+        N = fo.fir_ols_choose_n(M)
         assert N == want, (M, N, want)
         assert N >= max(M, 256) and N & (N - 1) == 0
 
@@ -39,6 +38,7 @@ def test_choice_arguments():
     with pytest.raises(fo.FirOlsError) as e:
         fo.fir_ols_choose_n(0)
     assert e.value.status == -1
-    assert fo.fir_ols_choose_n(65536, True) == 65536
-    with pytest.raises(fo.FirOlsError):
-        fo.fir_ols_choose_n(65537, True)
+    assert fo.fir_ols_choose_n(65536) == 65536
+    with pytest.raises(fo.FirOlsError) as e:
+        fo.fir_ols_choose_n(65537)
+    assert e.value.status == -2
