@@ -52,6 +52,9 @@ def parse():
                          "and output, copies overlapped with filtering); adds host_stream")
     ap.add_argument("--chunk", type=int, default=0,
                     help="samples per channel per step of the host-resident call (0: default)")
+    ap.add_argument("--real", action="store_true",
+                    help="also time real-valued input (two real rows per channel of the "
+                         "workload, 8 B per real sample); adds real_pairs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -376,6 +379,58 @@ def host_stream(args, inp, fo, torch, stream):
             "note": "includes the host link; never the headline value"}
 
 
+def real_pairs(inp, fo, torch, stream, nsets):
+    """Real-valued input on the workload's shape: each complex channel
+    becomes two real float32 rows of N(0,1) samples (seeded), filtered by
+    the workload's real taps through fir_ols_execute_real, with the same
+    calls per step.  Algorithmic bytes: 4 read + 4 written per real sample."""
+    w = inp.workload
+    if inp.taps is None or w.N > 16384:
+        return {"skipped": "needs real taps and N <= 16384"}
+    rng = np.random.default_rng(20261202 + 100 + w.nchan)
+    rows = torch.from_numpy(rng.standard_normal((2 * w.nchan, w.samples)).astype(np.float32))
+    xs = [rows.to("cuda:0") for _ in range(nsets)]
+    ys = [torch.empty_like(xs[0]) for _ in range(nsets)]
+    sptr = stream.cuda_stream
+    plan = fo.Plan(w.M, w.N, w.nchan)
+    plan.set_taps(inp.taps)
+
+    def rstep(k):
+        x, y = xs[k % nsets], ys[k % nsets]
+        pos = 0
+        for c in w.calls:
+            fo.fir_ols_execute_real(plan.handle, x.data_ptr() + 4 * pos, y.data_ptr() + 4 * pos,
+                                    c, w.samples, sptr)
+            pos += c
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for k in range(5):
+        rstep(k)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    rstep(0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    reps = max(20, int(1000.0 / max(e0.elapsed_time(e1), 1e-3)))
+    for k in range(reps):
+        rstep(k)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for k in range(reps):
+        rstep(k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    plan.close()
+    samples = 2 * w.nchan * w.samples
+    value = samples / (ms * 1e-3) / 1e6
+    roof = HBM_PEAK_GBPS * 1e9 / 8 / 1e6
+    return {"value": round(value, 1), "unit": "real Msamples/s", "ms_per_step": round(ms, 5),
+            "steps": reps, "bytes_per_sample": 8, "roof_Msamples": roof,
+            "hbm_roof_fraction": round(value / roof, 4),
+            "rows": 2 * w.nchan, "samples_per_row": w.samples}
+
+
 def valu_line(workload: str, kern_ms: float):
     """fp32 VALU throughput of the filtering kernel: counted flops per
     launch (committed counter run of the same sources) over the live
@@ -547,6 +602,7 @@ def main():
 
     plan.close()
     host = host_stream(args, inp, fo, torch, stream) if args.host_stream else None
+    real = real_pairs(inp, fo, torch, stream, nsets) if args.real else None
     out = {
         "metric": "filtered output Msamples/s (complex fp32) and % of HBM roof, per (M,N)",
         "value": round(value, 1),
@@ -583,6 +639,7 @@ def main():
         "valu": valu_line(w.key, kern_ms),
         "copy_reference_GBps": round(copy_gbps, 1),
         "host_stream": host,
+        "real_pairs": real,
         "parity": parity,
         "cpu_baseline": base,
         "wall_s": round(wall, 3),

@@ -131,6 +131,26 @@ int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev,
                     int64_t nsamples, int64_t chan_stride, void *stream);
 
 /*
+ * Real-valued input (the samples of page 2's data are real float32): two real
+ * streams filtered by a real filter at once.  Channel c of the plan is the
+ * pair of real rows 2c and 2c + 1:
+ *   x_dev, y_dev  device float32 [2 nchan][row_stride] (4-byte aligned).
+ * Row 2c goes in as the real and row 2c + 1 as the imaginary part of one
+ * complex stream; with real taps the real and imaginary parts of the
+ * output are the two filtered rows, written to rows 2c and 2c + 1 of y.  A
+ * real sample then moves 8 bytes (4 read, 4 written) against 16 for a
+ * complex one.  The state is the plan's complex state (real part: row 2c's
+ * last M-1 samples, imaginary part: row 2c + 1's), so fir_ols_set_state
+ * and fir_ols_get_state hold the two rows' states packed the same way.
+ * Stream-ordered and asynchronous like fir_ols_execute.
+ * FIR_OLS_ERR_UNSUPPORTED unless the filter was set by fir_ols_set_taps
+ * with real taps and N <= 16384; FIR_OLS_ERR_ALIGN for pointers not 4-byte
+ * aligned; other errors as fir_ols_execute.
+ */
+int fir_ols_execute_real(fir_ols_plan_t p, const void *x_dev, void *y_dev,
+                         int64_t nsamples, int64_t row_stride, void *stream);
+
+/*
  * Host-resident streaming (claim 1, steps 2 and 6: the samples arrive from
  * host memory in chunks and the filtered chunks go back to it).  Filters
  * nsamples per channel exactly as fir_ols_execute would, carrying the

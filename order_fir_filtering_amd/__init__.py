@@ -23,15 +23,17 @@ from .build import LIB as LIBRARY_PATH
 __all__ = [
     "FirOlsError", "Plan", "load_library", "LIBRARY_PATH", "EXPORTED",
     "fir_ols_plan", "fir_ols_set_taps", "fir_ols_set_freq_response",
-    "fir_ols_execute", "fir_ols_execute_host", "fir_ols_set_state", "fir_ols_get_state",
-    "fir_ols_destroy", "fir_ols_block_length", "fir_ols_choose_n", "fir_ols_status_string",
+    "fir_ols_execute", "fir_ols_execute_host", "fir_ols_execute_real", "fir_ols_set_state",
+    "fir_ols_get_state", "fir_ols_destroy", "fir_ols_block_length", "fir_ols_choose_n",
+    "fir_ols_status_string",
 ]
 
 # Every symbol include/firols.h declares.
 EXPORTED = (
     "fir_ols_plan", "fir_ols_set_taps", "fir_ols_set_freq_response",
-    "fir_ols_execute", "fir_ols_execute_host", "fir_ols_set_state", "fir_ols_get_state",
-    "fir_ols_destroy", "fir_ols_block_length", "fir_ols_choose_n", "fir_ols_status_string",
+    "fir_ols_execute", "fir_ols_execute_host", "fir_ols_execute_real", "fir_ols_set_state",
+    "fir_ols_get_state", "fir_ols_destroy", "fir_ols_block_length", "fir_ols_choose_n",
+    "fir_ols_status_string",
 )
 
 STATUS = {
@@ -70,6 +72,7 @@ def load_library(path: Optional[str] = None):
         "fir_ols_set_freq_response": (_int, [_vp, _vp, _i64, _vp]),
         "fir_ols_execute": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
         "fir_ols_execute_host": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+        "fir_ols_execute_real": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
         "fir_ols_set_state": (_int, [_vp, _vp, _vp]),
         "fir_ols_get_state": (_int, [_vp, _vp, _vp]),
         "fir_ols_destroy": (_int, [_vp]),
@@ -143,6 +146,13 @@ def fir_ols_execute(plan: int, x, y, nsamples: int, chan_stride: int, stream=Non
     lib = load_library()
     _check(lib.fir_ols_execute(plan, _ptr(x), _ptr(y), nsamples, chan_stride, _stream(stream)),
            "fir_ols_execute")
+
+
+def fir_ols_execute_real(plan: int, x, y, nsamples: int, row_stride: int, stream=None) -> None:
+    """Enqueue one call on real float32 rows ([2 nchan][row_stride] device buffers)."""
+    lib = load_library()
+    _check(lib.fir_ols_execute_real(plan, _ptr(x), _ptr(y), nsamples, row_stride,
+                                    _stream(stream)), "fir_ols_execute_real")
 
 
 def fir_ols_execute_host(plan: int, x, y, nsamples: int, chan_stride: int, chunk: int = 0,

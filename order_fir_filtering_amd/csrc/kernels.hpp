@@ -64,7 +64,10 @@ int fused_geometry(int logn);
 // never launches more.
 int fused_max_groups(int logn, int device);
 // Filter one call (steps 3-5 of the method and the state carry).
-hipError_t launch_fused(int logn, const FusedArgs &a, int max_groups, hipStream_t stream);
+// real: the channels are pairs of real float32 rows (a.x, a.y point to
+// [2 nchan][a.stride] floats), filtered by a real response.
+hipError_t launch_fused(int logn, const FusedArgs &a, int max_groups, hipStream_t stream,
+                        bool real = false);
 // H[i] = DFT_N(taps)[perm[i]] / N from N zero-padded complex taps.
 hipError_t launch_plan_taps(int logn, const float2 *taps_padded, float2 *H,
                             const float2 *tw, hipStream_t stream);

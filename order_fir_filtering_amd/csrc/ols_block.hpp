@@ -143,11 +143,41 @@ __device__ __forceinline__ void buf_store_cached(float2 v, __amdgpu_buffer_rsrc_
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(decltype(
         __builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, voff, soff, 0);
 }
+// Input of channel c as complex samples.  With REAL the channel is a pair
+// of real rows, 2c and 2c + 1 of a float32 [2 nchan][stride] array, whose
+// samples are the real and imaginary parts (two real streams filtered by a
+// real filter at once: the real and imaginary parts of the output are the
+// two filtered streams).
+template <bool REAL>
+struct ChanIn {
+    const float2 *__restrict__ xc;
+    const float *__restrict__ x1;
+    const float *__restrict__ x2;
+    __device__ __forceinline__ ChanIn(const FusedArgs &A, int64_t c)
+        : xc(A.x + c * A.stride),
+          x1((const float *)A.x + 2 * c * A.stride),
+          x2((const float *)A.x + (2 * c + 1) * A.stride) {}
+    __device__ __forceinline__ float2 operator[](int64_t g) const {
+        if constexpr (REAL)
+            return make_float2(x1[g], x2[g]);
+        else
+            return xc[g];
+    }
+};
+
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 2));
+}
+__device__ __forceinline__ void buf_store_f32(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, voff, 0, kStoreNT);
+}
+
 // State carry: the last M-1 samples of {S0, x} of channel c go to the new
-// state buffer (TB threads of the block that ends the channel).
-template <int GID>
-__device__ __forceinline__ void carry_state(int64_t nsamples, int Mm1, int tb,
-                                            const float2 *__restrict__ xc,
+// state buffer (TB threads of the block that ends the channel); xc[g] is
+// the channel's sample g (a pointer or a ChanIn).
+template <int GID, class XC>
+__device__ __forceinline__ void carry_state(int64_t nsamples, int Mm1, int tb, const XC &xc,
                                             const float2 *__restrict__ sc,
                                             float2 *__restrict__ sn) {
     constexpr Geo G = make_geo(GID);
@@ -166,12 +196,15 @@ __device__ __forceinline__ void carry_state(int64_t nsamples, int Mm1, int tb,
 // point: one over the valid input, one over the state), which keeps the
 // per-point address registers of large P out of the kernel.
 // NT selects the input loads' cache policy; R0 .. R1 selects the
-// registers to fill (default: all).
-template <int GID, bool BUF_EDGE = false, bool NT = true, int R0 = 0, int R1 = make_geo(GID).P>
+// registers to fill (default: all); REAL reads a pair of real rows per
+// channel (see ChanIn).
+template <int GID, bool BUF_EDGE = false, bool NT = true, int R0 = 0, int R1 = make_geo(GID).P,
+          bool REAL = false>
 __device__ __forceinline__ void gather_block_wave(const FusedArgs &A, int64_t gb, int tb,
                                                   float2 (&a)[make_geo(GID).P]) {
     constexpr Geo G = make_geo(GID);
     static_assert(G.TB % 64 == 0, "one block per wave or more");
+    static_assert(!(REAL && BUF_EDGE), "real pairs take the pointer edge path");
     const int64_t total = A.nblk * A.nchan;
     const bool active = gb < total;
     const int64_t c = active ? gb / A.nblk : 0;
@@ -180,6 +213,34 @@ __device__ __forceinline__ void gather_block_wave(const FusedArgs &A, int64_t gb
     const float2 *__restrict__ xc = A.x + c * A.stride;
     const float2 *__restrict__ sc = A.s0_old + c * Mm1;
     const int64_t g0 = i * A.L - Mm1;
+    if constexpr (REAL) {
+        const ChanIn<true> xr(A, c);
+        if (active && g0 >= 0 && g0 + G.N <= A.nsamples) {
+            // interior block: two 4-byte loads per point, one per row
+            const __amdgpu_buffer_rsrc_t r1 = buf_rsrc(xr.x1 + g0, G.N * 4u);
+            const __amdgpu_buffer_rsrc_t r2 = buf_rsrc(xr.x2 + g0, G.N * 4u);
+            const uint32_t vo = (uint32_t)tb * 4u;
+            static_for<R0, R1>([&](auto Rr) {
+                constexpr int r = decltype(Rr)::value;
+                constexpr uint32_t so = (uint32_t)(G.TB * pass0_m<GID>(r) * 4);
+                a[r] = make_float2(buf_load_f32(r1, vo, so), buf_load_f32(r2, vo, so));
+            });
+        } else {
+            static_for<R0, R1>([&](auto Rr) {
+                constexpr int r = decltype(Rr)::value;
+                const int64_t g = g0 + tb + G.TB * pass0_m<GID>(r);
+                float2 v = make_float2(0.f, 0.f);
+                if (active) {
+                    if (g < 0)
+                        v = sc[Mm1 + g];
+                    else if (g < A.nsamples)
+                        v = xr[g];
+                }
+                a[r] = v;
+            });
+        }
+        return;
+    }
     if (active && g0 >= 0 && g0 + G.N <= A.nsamples) {
         // interior block: one load per point, constant offsets in SGPRs
         const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc + g0, G.N * 8u);
@@ -228,7 +289,7 @@ __device__ __forceinline__ void gather_block_wave(const FusedArgs &A, int64_t gb
 // come from positions q = M-1 .. N-1; the descriptor covers the valid
 // outputs only, so the dropped positions (negative offset) and those past
 // the end fall outside it.
-template <int GID>
+template <int GID, bool REAL = false>
 __device__ __forceinline__ void store_block_wave(const FusedArgs &A, int64_t gb, int tb,
                                                  const float2 (&a)[make_geo(GID).P]) {
     constexpr Geo G = make_geo(GID);
@@ -240,15 +301,29 @@ __device__ __forceinline__ void store_block_wave(const FusedArgs &A, int64_t gb,
     int64_t yn = active ? A.nsamples - i * A.L : 0;
     if (yn > A.L) yn = A.L;
     if (yn < 0) yn = 0;
-    const __amdgpu_buffer_rsrc_t ry = buf_rsrc(A.y + c * A.stride + i * A.L, (uint32_t)yn * 8u);
-    static_for<0, G.P>([&](auto Rr) {
-        constexpr int r = decltype(Rr)::value;
-        const int q = tb + G.TB * pass0_m<GID>(r);
-        buf_store(a[r], ry, (uint32_t)(q - Mm1) * 8u);
-    });
+    if constexpr (REAL) {
+        // the real part to row 2c, the imaginary part to row 2c + 1
+        float *y1 = (float *)A.y + 2 * c * A.stride + i * A.L;
+        const __amdgpu_buffer_rsrc_t r1 = buf_rsrc(y1, (uint32_t)yn * 4u);
+        const __amdgpu_buffer_rsrc_t r2 = buf_rsrc(y1 + A.stride, (uint32_t)yn * 4u);
+        static_for<0, G.P>([&](auto Rr) {
+            constexpr int r = decltype(Rr)::value;
+            const int q = tb + G.TB * pass0_m<GID>(r);
+            buf_store_f32(a[r].x, r1, (uint32_t)(q - Mm1) * 4u);
+            buf_store_f32(a[r].y, r2, (uint32_t)(q - Mm1) * 4u);
+        });
+    } else {
+        const __amdgpu_buffer_rsrc_t ry =
+            buf_rsrc(A.y + c * A.stride + i * A.L, (uint32_t)yn * 8u);
+        static_for<0, G.P>([&](auto Rr) {
+            constexpr int r = decltype(Rr)::value;
+            const int q = tb + G.TB * pass0_m<GID>(r);
+            buf_store(a[r], ry, (uint32_t)(q - Mm1) * 8u);
+        });
+    }
 
     if (active && i == A.nblk - 1)
-        carry_state<GID>(A.nsamples, Mm1, tb, A.x + c * A.stride, A.s0_old + c * Mm1,
+        carry_state<GID>(A.nsamples, Mm1, tb, ChanIn<REAL>(A, c), A.s0_old + c * Mm1,
                          A.s0_new + c * Mm1);
 }
 

@@ -43,24 +43,23 @@ struct FusedCfg {
 // block.  Inactive threads (padding sub-blocks) take part in the barriers.
 // This form serves blocks smaller than a wavefront (several blocks share a
 // wave), with plain pointer accesses.
-template <int GID, class TW, class HP>
+template <int GID, bool REAL, class TW, class HP>
 __device__ __forceinline__ void filter_block(const FusedArgs &A, int64_t gb, bool active, int tb,
                                              float2 *my, const TW &tw, const HP &hp) {
     constexpr Geo G = make_geo(GID);
     const int64_t c = active ? gb / A.nblk : 0;
     const int64_t i = active ? gb - c * A.nblk : 0;
     const int Mm1 = A.M - 1;
-    const float2 *__restrict__ xc = A.x + c * A.stride;
+    const ChanIn<REAL> xc(A, c);
     const float2 *__restrict__ sc = A.s0_old + c * Mm1;
 
     // E_i[q] = xt[i L - (M-1) + q], xt = {S0, x, zeros}.
     float2 a[G.P];
     const int64_t g0 = i * A.L - Mm1;
     if (active && g0 >= 0 && g0 + G.N <= A.nsamples) {
-        const float2 *__restrict__ xb = xc + g0 + tb;
         static_for<0, G.P>([&](auto Rr) {
             constexpr int r = decltype(Rr)::value;
-            a[r] = xb[G.TB * pass0_m<GID>(r)];
+            a[r] = xc[g0 + tb + G.TB * pass0_m<GID>(r)];
         });
     } else {
         static_for<0, G.P>([&](auto Rr) {
@@ -85,18 +84,32 @@ __device__ __forceinline__ void filter_block(const FusedArgs &A, int64_t gb, boo
     if (!active) return;
 
     // Position q >= M-1 is output i L + q - (M-1).
-    float2 *__restrict__ yb = A.y + c * A.stride + g0 + tb;
     const int64_t lim = A.nsamples - g0 - tb;   // q - tb must stay below this
-    static_for<0, G.P>([&](auto Rr) {
-        constexpr int r = decltype(Rr)::value;
-        constexpr int off = G.TB * pass0_m<GID>(r);
-        if (tb + off >= Mm1 && off < lim) yb[off] = a[r];
-    });
+    if constexpr (REAL) {
+        // the real part to row 2c, the imaginary part to row 2c + 1
+        float *__restrict__ y1 = (float *)A.y + 2 * c * A.stride + g0 + tb;
+        float *__restrict__ y2 = y1 + A.stride;
+        static_for<0, G.P>([&](auto Rr) {
+            constexpr int r = decltype(Rr)::value;
+            constexpr int off = G.TB * pass0_m<GID>(r);
+            if (tb + off >= Mm1 && off < lim) {
+                y1[off] = a[r].x;
+                y2[off] = a[r].y;
+            }
+        });
+    } else {
+        float2 *__restrict__ yb = A.y + c * A.stride + g0 + tb;
+        static_for<0, G.P>([&](auto Rr) {
+            constexpr int r = decltype(Rr)::value;
+            constexpr int off = G.TB * pass0_m<GID>(r);
+            if (tb + off >= Mm1 && off < lim) yb[off] = a[r];
+        });
+    }
 
     if (i == A.nblk - 1) carry_state<GID>(A.nsamples, Mm1, tb, xc, sc, A.s0_new + c * Mm1);
 }
 
-template <int GID, class TW, class HP>
+template <int GID, bool REAL, class TW, class HP>
 __device__ __forceinline__ void process_block_wave(const FusedArgs &A, int64_t gb, int tb,
                                                    float2 (&a)[make_geo(GID).P], float2 *my,
                                                    const TW &tw, const HP &hp) {
@@ -104,10 +117,11 @@ __device__ __forceinline__ void process_block_wave(const FusedArgs &A, int64_t g
     mul_h<GID>(a, hp);
     inverse_all<GID>(tb, a, my, tw);
 
-    store_block_wave<GID>(A, gb, tb, a);
+    store_block_wave<GID, REAL>(A, gb, tb, a);
 }
 
-template <int GID>
+// REAL: each channel is a pair of real float32 rows (see ChanIn).
+template <int GID, bool REAL>
 __global__ __launch_bounds__(FusedCfg<GID>::WG, FusedCfg<GID>::MIN_WAVES_PER_SIMD) void ols_fused_kernel(
     FusedArgs A) {
     using C = FusedCfg<GID>;
@@ -127,7 +141,7 @@ __global__ __launch_bounds__(FusedCfg<GID>::WG, FusedCfg<GID>::MIN_WAVES_PER_SIM
             const int64_t unit = unit_of(units, blockIdx.x, gridDim.x, it);
             if (unit < 0) break;
             const int64_t gb = unit * C::BPW + sub;
-            filter_block<GID>(A, gb, gb < total, tb, my, tw, hp);
+            filter_block<GID, REAL>(A, gb, gb < total, tb, my, tw, hp);
         }
     };
     if constexpr (C::WAVE_IO && C::REGS) {
@@ -136,15 +150,15 @@ __global__ __launch_bounds__(FusedCfg<GID>::WG, FusedCfg<GID>::MIN_WAVES_PER_SIM
         // later blocks' inputs are requested right after the stores
         float2 a[G.P];
         int64_t unit = unit_of(units, blockIdx.x, gridDim.x, 0);
-        if (unit >= 0) gather_block_wave<GID>(A, unit * C::BPW + sub, tb, a);
+        if (unit >= 0) gather_block_wave<GID, false, true, 0, G.P, REAL>(A, unit * C::BPW + sub, tb, a);
         TwRegs<GID> tw;
         tw.load(A.tw, tb);
         HRegs<GID> hp;
         hp.load(A.H, tb);
         for (int64_t it = 1; unit >= 0; ++it) {
-            process_block_wave<GID>(A, unit * C::BPW + sub, tb, a, my, tw, hp);
+            process_block_wave<GID, REAL>(A, unit * C::BPW + sub, tb, a, my, tw, hp);
             unit = unit_of(units, blockIdx.x, gridDim.x, it);
-            if (unit >= 0) gather_block_wave<GID>(A, unit * C::BPW + sub, tb, a);
+            if (unit >= 0) gather_block_wave<GID, false, true, 0, G.P, REAL>(A, unit * C::BPW + sub, tb, a);
         }
     } else if constexpr (C::WAVE_IO) {
         for (int64_t it = 0;; ++it) {
@@ -155,8 +169,8 @@ __global__ __launch_bounds__(FusedCfg<GID>::WG, FusedCfg<GID>::MIN_WAVES_PER_SIM
             asm volatile("" : "+s"(twp), "+s"(hpp));
             const int64_t gb = unit * C::BPW + sub;
             float2 a[G.P];
-            gather_block_wave<GID>(A, gb, tb, a);
-            process_block_wave<GID>(A, gb, tb, a, my, TwTable<GID>{twp, tb}, HTable<GID>{hpp, tb});
+            gather_block_wave<GID, false, true, 0, G.P, REAL>(A, gb, tb, a);
+            process_block_wave<GID, REAL>(A, gb, tb, a, my, TwTable<GID>{twp, tb}, HTable<GID>{hpp, tb});
         }
     } else if constexpr (C::REGS) {
         TwRegs<GID> tw;
@@ -175,7 +189,7 @@ __global__ __launch_bounds__(FusedCfg<GID>::WG, FusedCfg<GID>::MIN_WAVES_PER_SIM
             const float2 *hpp = A.H;
             asm volatile("" : "+s"(twp), "+s"(hpp));
             const int64_t gb = unit * C::BPW + sub;
-            filter_block<GID>(A, gb, gb < total, tb, my, TwTable<GID>{twp, tb},
+            filter_block<GID, REAL>(A, gb, gb < total, tb, my, TwTable<GID>{twp, tb},
                               HTable<GID>{hpp, tb});
         }
     }
@@ -215,7 +229,8 @@ constexpr int fused_gid(int logn) { return logn; }
 int fused_geometry(int logn) { return fused_gid(logn); }
 
 template <int GID>
-static hipError_t launch_fused_t(const FusedArgs &a, int max_groups, hipStream_t stream) {
+static hipError_t launch_fused_t(const FusedArgs &a, int max_groups, hipStream_t stream,
+                                 bool real) {
     using C = FusedCfg<GID>;
     const int64_t total = a.nblk * a.nchan;
     const int64_t units = (total + C::BPW - 1) / C::BPW;
@@ -223,7 +238,12 @@ static hipError_t launch_fused_t(const FusedArgs &a, int max_groups, hipStream_t
     int64_t grid = units;
     if (grid > max_groups) grid = max_groups & ~7;    // persistent, multiple of 8
     if (grid <= 0) grid = units < max_groups ? units : max_groups;
-    hipLaunchKernelGGL(ols_fused_kernel<GID>, dim3((unsigned)grid), dim3(C::WG), 0, stream, a);
+    if (real)
+        hipLaunchKernelGGL((ols_fused_kernel<GID, true>), dim3((unsigned)grid), dim3(C::WG), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((ols_fused_kernel<GID, false>), dim3((unsigned)grid), dim3(C::WG), 0,
+                           stream, a);
     return hipGetLastError();
 }
 
@@ -235,32 +255,39 @@ static hipError_t launch_plan_t(const float2 *taps, float2 *H, const float2 *tw,
     return hipGetLastError();
 }
 
-hipError_t launch_fused(int logn, const FusedArgs &a, int max_groups, hipStream_t stream) {
+hipError_t launch_fused(int logn, const FusedArgs &a, int max_groups, hipStream_t stream,
+                        bool real) {
     switch (logn) {
-        case 3: return launch_fused_t<fused_gid(3)>(a, max_groups, stream);
-        case 4: return launch_fused_t<fused_gid(4)>(a, max_groups, stream);
-        case 5: return launch_fused_t<fused_gid(5)>(a, max_groups, stream);
-        case 6: return launch_fused_t<fused_gid(6)>(a, max_groups, stream);
-        case 7: return launch_fused_t<fused_gid(7)>(a, max_groups, stream);
-        case 8: return launch_fused_t<fused_gid(8)>(a, max_groups, stream);
-        case 9: return launch_fused_t<fused_gid(9)>(a, max_groups, stream);
-        case 10: return launch_fused_t<fused_gid(10)>(a, max_groups, stream);
-        case 11: return launch_fused_t<fused_gid(11)>(a, max_groups, stream);
-        case 12: return launch_fused_t<fused_gid(12)>(a, max_groups, stream);
-        case 13: return launch_fused_t<fused_gid(13)>(a, max_groups, stream);
-        case 14: return launch_fused_t<fused_gid(14)>(a, max_groups, stream);
+        case 3: return launch_fused_t<fused_gid(3)>(a, max_groups, stream, real);
+        case 4: return launch_fused_t<fused_gid(4)>(a, max_groups, stream, real);
+        case 5: return launch_fused_t<fused_gid(5)>(a, max_groups, stream, real);
+        case 6: return launch_fused_t<fused_gid(6)>(a, max_groups, stream, real);
+        case 7: return launch_fused_t<fused_gid(7)>(a, max_groups, stream, real);
+        case 8: return launch_fused_t<fused_gid(8)>(a, max_groups, stream, real);
+        case 9: return launch_fused_t<fused_gid(9)>(a, max_groups, stream, real);
+        case 10: return launch_fused_t<fused_gid(10)>(a, max_groups, stream, real);
+        case 11: return launch_fused_t<fused_gid(11)>(a, max_groups, stream, real);
+        case 12: return launch_fused_t<fused_gid(12)>(a, max_groups, stream, real);
+        case 13: return launch_fused_t<fused_gid(13)>(a, max_groups, stream, real);
+        case 14: return launch_fused_t<fused_gid(14)>(a, max_groups, stream, real);
         default: return hipErrorInvalidValue;
     }
 }
 
+// Resident workgroups per CU of both variants (complex and real-pair
+// channels), the smaller of the two.
 template <int GID>
 static int max_groups_t(int cus) {
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ols_fused_kernel<GID>,
+    int pc = 0, pr = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&pc, ols_fused_kernel<GID, false>,
                                                      FusedCfg<GID>::WG, 0) != hipSuccess ||
-        per_cu < 1)
-        per_cu = 1;
-    return per_cu * cus;
+        pc < 1)
+        pc = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&pr, ols_fused_kernel<GID, true>,
+                                                     FusedCfg<GID>::WG, 0) != hipSuccess ||
+        pr < 1)
+        pr = 1;
+    return (pc < pr ? pc : pr) * cus;
 }
 
 int fused_max_groups(int logn, int device) {

@@ -167,7 +167,9 @@ int fir_ols_set_taps(fir_ols_plan_t p, const float *h_host, int64_t M, int is_co
             H[2 * q] = (float)a[q].real();
             H[2 * q + 1] = (float)a[q].imag();
         }
-        return upload_freq_response(p, H.data(), (hipStream_t)stream);
+        const int st = upload_freq_response(p, H.data(), (hipStream_t)stream);
+        if (st == FIR_OLS_OK) p->real_filter = !is_complex;
+        return st;
     }
     std::vector<float2> padded((size_t)p->N, make_float2(0.f, 0.f));
     for (int64_t m = 0; m < M; ++m)
@@ -182,13 +184,16 @@ int fir_ols_set_taps(fir_ols_plan_t p, const float *h_host, int64_t M, int is_co
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return FIR_OLS_ERR_HIP;
     p->has_filter = true;
+    p->real_filter = !is_complex;
     return FIR_OLS_OK;
 }
 
 int fir_ols_set_freq_response(fir_ols_plan_t p, const float *H_host, int64_t N, void *stream) {
     if (!p || !H_host || N != p->N) return FIR_OLS_ERR_INVALID_ARG;
     if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
-    return upload_freq_response(p, H_host, (hipStream_t)stream);
+    const int st = upload_freq_response(p, H_host, (hipStream_t)stream);
+    if (st == FIR_OLS_OK) p->real_filter = false;
+    return st;
 }
 
 }  // extern "C"
@@ -270,6 +275,40 @@ int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev, int64_t ns
         e = is_big(p) ? firols::launch_big(a, p->max_groups, (hipStream_t)stream)
                       : firols::launch_fused(p->logn, a, p->max_groups, (hipStream_t)stream);
     }
+    if (e != hipSuccess) return FIR_OLS_ERR_HIP;
+    if (p->M > 1) p->parity ^= 1;
+    return FIR_OLS_OK;
+}
+
+int fir_ols_execute_real(fir_ols_plan_t p, const void *x_dev, void *y_dev, int64_t nsamples,
+                         int64_t row_stride, void *stream) {
+    if (!p || nsamples < 0) return FIR_OLS_ERR_INVALID_ARG;
+    if (!p->has_filter) return FIR_OLS_ERR_NO_FILTER;
+    if (!p->real_filter || p->logn > firols::kFusedMaxLogN) return FIR_OLS_ERR_UNSUPPORTED;
+    if (nsamples == 0) return FIR_OLS_OK;
+    if (!x_dev || !y_dev || row_stride < nsamples) return FIR_OLS_ERR_INVALID_ARG;
+    if (((uintptr_t)x_dev | (uintptr_t)y_dev) & 3) return FIR_OLS_ERR_ALIGN;
+    if (row_stride > ((int64_t)1 << 50) / (2 * p->nchan)) return FIR_OLS_ERR_INVALID_ARG;
+    const int64_t span = ((2 * p->nchan - 1) * row_stride + nsamples) * (int64_t)sizeof(float);
+    const uintptr_t xa = (uintptr_t)x_dev, ya = (uintptr_t)y_dev;
+    if (xa < ya + (uintptr_t)span && ya < xa + (uintptr_t)span) return FIR_OLS_ERR_ALIAS;
+    if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
+
+    firols::FusedArgs a;
+    a.x = (const float2 *)x_dev;   // read as float32 rows by the real-pair kernels
+    a.y = (float2 *)y_dev;
+    a.s0_old = p->state[p->parity];
+    a.s0_new = p->state[p->parity ^ 1];
+    a.H = p->H;
+    a.tw = p->tw;
+    a.nsamples = nsamples;
+    a.stride = row_stride;
+    a.nblk = (nsamples + p->L - 1) / p->L;
+    a.M = (int)p->M;
+    a.L = (int)p->L;
+    a.nchan = (int)p->nchan;
+    const hipError_t e =
+        firols::launch_fused(p->logn, a, p->max_groups, (hipStream_t)stream, /*real=*/true);
     if (e != hipSuccess) return FIR_OLS_ERR_HIP;
     if (p->M > 1) p->parity ^= 1;
     return FIR_OLS_OK;

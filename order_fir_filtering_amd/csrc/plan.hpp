@@ -17,6 +17,7 @@ struct fir_ols_plan_s {
     int parity = 0;               // state[parity] is the current state
     int max_groups = 0;           // resident workgroups of the filtering kernel
     bool has_filter = false;
+    bool real_filter = false;     // the filter came from real taps (set_taps, is_complex == 0)
     // split path (N = 65536)
     float2 *tw_top = nullptr;     // W_N^{q k0}, k0 = 0 .. RT-1
     float2 *scratch = nullptr;    // max_groups slots of N values
