@@ -146,8 +146,7 @@ __global__ __launch_bounds__(FusedCfg<GID>::WG, FusedCfg<GID>::MIN_WAVES_PER_SIM
     };
     if constexpr (C::WAVE_IO && C::REGS) {
         // the first block's input is requested before the register-held
-        // twiddles and H, so the first pass only waits for its own data;
-        // later blocks' inputs are requested right after the stores
+        // twiddles and H, so the first pass only waits for its own data
         float2 a[G.P];
         int64_t unit = unit_of(units, blockIdx.x, gridDim.x, 0);
         if (unit >= 0) gather_block_wave<GID, false, true, 0, G.P, REAL>(A, unit * C::BPW + sub, tb, a);
@@ -155,10 +154,27 @@ __global__ __launch_bounds__(FusedCfg<GID>::WG, FusedCfg<GID>::MIN_WAVES_PER_SIM
         tw.load(A.tw, tb);
         HRegs<GID> hp;
         hp.load(A.H, tb);
-        for (int64_t it = 1; unit >= 0; ++it) {
+        if (units <= (int64_t)gridDim.x) {
+            // one block per workgroup: nothing to request ahead
+            if (unit >= 0) process_block_wave<GID, REAL>(A, unit * C::BPW + sub, tb, a, my, tw, hp);
+            return;
+        }
+        // several blocks per workgroup: the next block's input is requested
+        // into a second register set before this block's transform, so its
+        // loads are in flight while the transform runs (a and b alternate;
+        // the transform itself issues no memory loads).  Measured on 1024
+        // channels at N = 1024: 290 -> 303 GS/s; one long call at N = 2048:
+        // 245 -> 268 GS/s.
+        float2 b[G.P];
+        for (int64_t it = 1; unit >= 0; it += 2) {
+            const int64_t u1 = unit_of(units, blockIdx.x, gridDim.x, it);
+            if (u1 >= 0) gather_block_wave<GID, false, true, 0, G.P, REAL>(A, u1 * C::BPW + sub, tb, b);
             process_block_wave<GID, REAL>(A, unit * C::BPW + sub, tb, a, my, tw, hp);
-            unit = unit_of(units, blockIdx.x, gridDim.x, it);
-            if (unit >= 0) gather_block_wave<GID, false, true, 0, G.P, REAL>(A, unit * C::BPW + sub, tb, a);
+            if (u1 < 0) break;
+            const int64_t u2 = unit_of(units, blockIdx.x, gridDim.x, it + 1);
+            if (u2 >= 0) gather_block_wave<GID, false, true, 0, G.P, REAL>(A, u2 * C::BPW + sub, tb, a);
+            process_block_wave<GID, REAL>(A, u1 * C::BPW + sub, tb, b, my, tw, hp);
+            unit = u2;
         }
     } else if constexpr (C::WAVE_IO) {
         for (int64_t it = 0;; ++it) {

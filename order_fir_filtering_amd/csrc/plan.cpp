@@ -351,9 +351,9 @@ int64_t fir_ols_choose_n(int64_t M) {
     // blocks per second of N = 2^8 .. 2^16 on MI355X, measured by
     // order_fir_filtering_amd/tune_n.py (one call of many blocks per N)
     static const double kBlocksPerSecond[] = {
-        1409070468.0, 695496558.7, 359583480.4,
-        159442253.4, 69565365.6, 21163666.1,
-        7907989.3, 6760967.2, 2208279.9};
+        1419658699.9, 711354696.3, 379209091.9,
+        173905752.5, 73544040.6, 21122692.5,
+        7899529.8, 7036289.6, 2221584.7};
     if (M < 1) return FIR_OLS_ERR_INVALID_ARG;
     int64_t best = FIR_OLS_ERR_UNSUPPORTED;
     double best_rate = 0.0;
