@@ -31,12 +31,16 @@ void free_slots(fir_ols_plan_s *p) {
 // a larger chunk is asked for).
 int prepare(fir_ols_plan_s *p, int64_t chunk) {
     if (!p->hs_in) {
-        if (hipStreamCreateWithFlags(&p->hs_in, hipStreamNonBlocking) != hipSuccess ||
-            hipStreamCreateWithFlags(&p->hs_out, hipStreamNonBlocking) != hipSuccess)
-            return FIR_OLS_ERR_HIP;
+        // all or nothing: a failure leaves no stream or event behind
+        bool ok = hipStreamCreateWithFlags(&p->hs_in, hipStreamNonBlocking) == hipSuccess &&
+                  hipStreamCreateWithFlags(&p->hs_out, hipStreamNonBlocking) == hipSuccess;
         for (hipEvent_t &e : p->hs_ev)
-            if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
-                return FIR_OLS_ERR_HIP;
+            ok = ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
+        if (!ok) {
+            (void)hipGetLastError();
+            release_host_stream(p);
+            return FIR_OLS_ERR_HIP;
+        }
     }
     if (chunk <= p->hs_chunk) return FIR_OLS_OK;
     // earlier calls may still read or write the old slots
