@@ -61,14 +61,16 @@ enum {
  * transform length, the block length is L = N - M + 1).
  *   out    receives the handle (set to NULL on error).
  *   M      taps, 1 <= M <= N.
- *   N      power of two, 8 <= N <= 65536.
+ *   N      power of two, 8 <= N <= 2^20 (1048576).
  *   nchan  independent channels sharing the filter, nchan >= 1; each has
  *          its own state.
  * Allocates the frequency response (aligned to 256 bytes, the page's
  * alignment rule in step 1), the twiddle tables and two state buffers of
  * nchan*(M-1) samples on the current device; for N = 65536 also a scratch
  * area of N samples (512 KB) per workgroup that fits on the device at once
- * (128 MiB on a 256-CU MI355X).  The state starts at zero.
+ * (128 MiB on a 256-CU MI355X), and for N > 65536 a scratch area of
+ * 128 MiB (blocks of N samples, at least one) through which the blocks of
+ * a call pass in batches.  The state starts at zero.
  * No filter is set yet.  Synchronous.
  */
 int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan);
@@ -76,7 +78,7 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan);
 /*
  * Set the filter from its taps (claim 1, step 1, first case): the taps are
  * zero-padded to N and transformed, on the GPU for N <= 32768 and on the
- * host in float64 for N = 65536; H is kept scaled by 1/N so the inverse
+ * host in float64 for N >= 65536; H is kept scaled by 1/N so the inverse
  * transform of step 4 needs no separate scaling.
  *   h_host      host array: M float32 taps (is_complex == 0) or M
  *               interleaved complex64 taps (is_complex != 0); copied
@@ -121,7 +123,8 @@ int fir_ols_set_freq_response(fir_ols_plan_t p, const float *H_host,
  * another block still reads).  The state of every channel becomes the last
  * M-1 samples of {S0, x} of that channel.
  * The call enqueues kernel launches only (no allocation, copy, fill or
- * synchronization), so a run of calls may be captured into a HIP graph;
+ * synchronization): one for N <= 65536, three per batch of blocks for
+ * N > 65536.  So a run of calls may be captured into a HIP graph;
  * replays then carry the state like the calls they were captured from,
  * provided the captured run has an even number of calls with M > 1 (the
  * two state buffers alternate, and the plan's record of which one is

@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfirols.so")
-SOURCES = ["plan.cpp", "host_stream.cpp", "ols_fused.hip", "ols_big.hip", "ols_split.hip"]
+SOURCES = ["plan.cpp", "host_stream.cpp", "ols_fused.hip", "ols_big.hip", "ols_split.hip",
+           "ols_multi.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

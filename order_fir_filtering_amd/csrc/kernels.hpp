@@ -41,11 +41,34 @@ struct SplitArgs {
     int nchan;
 };
 
+// Arguments of one batch of the multi-pass path (N = 2^17 .. 2^20): the
+// units (channel, block) u0 .. u0 + nu - 1 of a call, unit = c * nblk + i.
+struct MultiArgs {
+    const float2 *x;        // [nchan][stride] input
+    float2 *y;              // [nchan][stride] output
+    const float2 *s0_old;   // [nchan][M-1] state read by this call
+    float2 *s0_new;         // [nchan][M-1] state written by this call
+    const float2 *H;        // RT * Ns values: bins k0 + RT k' in sub-kernel order, / N
+    const float2 *tw;       // twiddle table of the Ns-point sub-transform
+    const float2 *tw_top;   // W_N^{q k0} factors: [RT][256] (q mod 256), then [RT][Ns/256]
+    float2 *scratch;        // [nu][RT][Ns]: the sub-sequences, then their convolutions
+    int64_t nsamples;       // samples per channel in this call (> 0)
+    int64_t stride;         // elements between channel starts
+    int64_t nblk;           // blocks per channel
+    int64_t u0;             // first unit of the batch
+    int nu;                 // units in the batch
+    int M;
+    int L;
+    int nchan;
+};
+
 // Largest log2(N) the LDS-resident kernel covers; N = 2^kBigLogN takes the
-// half-resident kernel, larger N (up to kMaxLogN) the split path.
+// half-resident kernel, N = 2^kSplitLogN the split path, larger N (up to
+// kMaxLogN) the multi-pass path.
 constexpr int kFusedMaxLogN = 14;
 constexpr int kBigLogN = 15;
-constexpr int kMaxLogN = 16;
+constexpr int kSplitLogN = 16;
+constexpr int kMaxLogN = 20;
 constexpr int kMinLogN = 3;
 
 // The table builders take a geometry id (geo_id(logn, logp)); a plain
@@ -88,6 +111,16 @@ void build_split_h_permutation(int logn, int64_t *perm);
 int64_t split_slot_elems(int logn);
 int split_max_groups(int device);
 hipError_t launch_split(int logn, const SplitArgs &a, int max_groups, hipStream_t stream);
+
+// Multi-pass path (N = 2^17 .. 2^20): top-pass twiddle table size and
+// builder (the sub-transform shares the split path's tables and H order),
+// units per batch for the plan's scratch, workgroups of the sub-transform
+// kernel, and one batch's three launches.
+int64_t multi_top_twiddle_count(int logn);
+void build_multi_top_twiddles(int logn, float2 *top_tw);
+int multi_batch_units(int logn);
+int multi_max_groups(int device);
+hipError_t launch_multi(int logn, const MultiArgs &a, int max_groups, hipStream_t stream);
 
 // dst[i] = src ? src[i] : 0 for i < count.
 hipError_t launch_copy(float2 *dst, const float2 *src, int64_t count,

@@ -45,8 +45,11 @@ void release(fir_ols_plan_s *p) {
 
 int64_t state_len(const fir_ols_plan_s *p) { return p->nchan * (p->M - 1); }
 
-bool is_split(const fir_ols_plan_s *p) { return p->logn > firols::kBigLogN; }
+bool is_multi(const fir_ols_plan_s *p) { return p->logn > firols::kSplitLogN; }
+bool is_split(const fir_ols_plan_s *p) { return p->logn == firols::kSplitLogN; }
 bool is_big(const fir_ols_plan_s *p) { return p->logn == firols::kBigLogN; }
+// split and multi-pass paths: H from the host, in the split order
+bool host_response(const fir_ols_plan_s *p) { return p->logn > firols::kBigLogN; }
 // geometry id of the plan's table builders (fused and half-resident paths)
 int table_geometry(const fir_ols_plan_s *p) {
     return is_big(p) ? firols::big_geometry() : firols::fused_geometry(p->logn);
@@ -103,14 +106,22 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
     p->N = N;
     p->L = N - M + 1;
     p->nchan = nchan;
-    const bool split = is_split(p);
-    p->max_groups = split       ? firols::split_max_groups(p->device)
+    const bool split = is_split(p), multi = is_multi(p);
+    p->max_groups = multi       ? firols::multi_max_groups(p->device)
+                    : split     ? firols::split_max_groups(p->device)
                     : is_big(p) ? firols::big_max_groups(p->device)
                                 : firols::fused_max_groups(logn, p->device);
     (void)hipGetLastError();
 
-    const int ntw = split ? firols::split_sub_twiddle_count() : firols::twiddle_count(table_geometry(p));
-    const int64_t ntop = split ? firols::split_top_twiddle_count(logn) : 0;
+    const int ntw = split || multi ? firols::split_sub_twiddle_count()
+                                   : firols::twiddle_count(table_geometry(p));
+    const int64_t ntop = multi   ? firols::multi_top_twiddle_count(logn)
+                         : split ? firols::split_top_twiddle_count(logn)
+                                 : 0;
+    const int64_t nscratch =
+        multi   ? (int64_t)firols::multi_batch_units(logn) * N
+        : split ? (int64_t)p->max_groups * firols::split_slot_elems(logn)
+                : 0;
     const size_t sbytes = (size_t)state_len(p) * sizeof(float2);
     bool ok = hipMalloc(&p->H, N * sizeof(float2)) == hipSuccess &&
               hipMalloc(&p->tw, (size_t)(ntw > 0 ? ntw : 1) * sizeof(float2)) == hipSuccess &&
@@ -119,10 +130,9 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
         ok = hipMalloc(&p->state[0], sbytes) == hipSuccess &&
              hipMalloc(&p->state[1], sbytes) == hipSuccess;
     }
-    if (ok && split) {
+    if (ok && (split || multi)) {
         ok = hipMalloc(&p->tw_top, (size_t)ntop * sizeof(float2)) == hipSuccess &&
-             hipMalloc(&p->scratch, (size_t)p->max_groups * (size_t)firols::split_slot_elems(logn) *
-                                        sizeof(float2)) == hipSuccess;
+             hipMalloc(&p->scratch, (size_t)nscratch * sizeof(float2)) == hipSuccess;
     }
     if (!ok) {
         (void)hipGetLastError();
@@ -132,12 +142,16 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
 
     std::vector<float2> tw((size_t)(ntw > 0 ? ntw : 1), make_float2(1.f, 0.f));
     std::vector<float2> top((size_t)(ntop > 0 ? ntop : 1));
-    if (split)
+    if (multi) {
+        firols::build_twiddles(firols::big_geometry(), tw.data());
+        firols::build_multi_top_twiddles(logn, top.data());
+    } else if (split) {
         firols::build_split_twiddles(logn, tw.data(), top.data());
-    else
+    } else {
         firols::build_twiddles(table_geometry(p), tw.data());
+    }
     hipError_t e = hipMemcpy(p->tw, tw.data(), tw.size() * sizeof(float2), hipMemcpyHostToDevice);
-    if (e == hipSuccess && split)
+    if (e == hipSuccess && (split || multi))
         e = hipMemcpy(p->tw_top, top.data(), (size_t)ntop * sizeof(float2), hipMemcpyHostToDevice);
     if (e == hipSuccess && sbytes) e = launch_copy(p->state[0], nullptr, state_len(p), nullptr);
     if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -154,9 +168,9 @@ int fir_ols_set_taps(fir_ols_plan_t p, const float *h_host, int64_t M, int is_co
                      void *stream) {
     if (!p || !h_host || M != p->M) return FIR_OLS_ERR_INVALID_ARG;
     if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
-    if (is_split(p)) {
-        // N = 65536: H is computed on the host (float64) and takes the
-        // frequency-response path; no planning kernel runs for this size
+    if (host_response(p)) {
+        // N >= 65536: H is computed on the host (float64) and takes the
+        // frequency-response path; no planning kernel runs for these sizes
         std::vector<std::complex<double>> a((size_t)p->N, 0.0);
         for (int64_t m = 0; m < M; ++m)
             a[m] = is_complex ? std::complex<double>(h_host[2 * m], h_host[2 * m + 1])
@@ -205,7 +219,7 @@ namespace {
 int upload_freq_response(fir_ols_plan_t p, const float *H_host, hipStream_t s) {
     const int64_t N = p->N;
     std::vector<int64_t> perm((size_t)N);
-    if (is_split(p))
+    if (host_response(p))
         firols::build_split_h_permutation(p->logn, perm.data());
     else
         firols::build_h_permutation(table_geometry(p), perm.data());
@@ -241,7 +255,26 @@ int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev, int64_t ns
 
     const int64_t nblk = (nsamples + p->L - 1) / p->L;
     hipError_t e = hipSuccess;
-    if (is_split(p)) {
+    if (is_multi(p)) {
+        firols::MultiArgs a;
+        a.x = (const float2 *)x_dev;
+        a.y = (float2 *)y_dev;
+        a.s0_old = p->state[p->parity];
+        a.s0_new = p->state[p->parity ^ 1];
+        a.H = p->H;
+        a.tw = p->tw;
+        a.tw_top = p->tw_top;
+        a.scratch = p->scratch;
+        a.nsamples = nsamples;
+        a.stride = chan_stride;
+        a.nblk = nblk;
+        a.u0 = 0;
+        a.nu = 0;
+        a.M = (int)p->M;
+        a.L = (int)p->L;
+        a.nchan = (int)p->nchan;
+        e = firols::launch_multi(p->logn, a, p->max_groups, (hipStream_t)stream);
+    } else if (is_split(p)) {
         firols::SplitArgs a;
         a.x = (const float2 *)x_dev;
         a.y = (float2 *)y_dev;

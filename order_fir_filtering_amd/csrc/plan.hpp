@@ -18,9 +18,9 @@ struct fir_ols_plan_s {
     int max_groups = 0;           // resident workgroups of the filtering kernel
     bool has_filter = false;
     bool real_filter = false;     // the filter came from real taps (set_taps, is_complex == 0)
-    // split path (N = 65536)
-    float2 *tw_top = nullptr;     // W_N^{q k0}, k0 = 0 .. RT-1
-    float2 *scratch = nullptr;    // max_groups slots of N values
+    // split path (N = 65536) and multi-pass path (N = 2^17 .. 2^20)
+    float2 *tw_top = nullptr;     // W_N^{q k0} (split: full rows; multi-pass: two factors)
+    float2 *scratch = nullptr;    // split: max_groups slots of N values; multi-pass: a batch of blocks
     // host-resident streaming (fir_ols_execute_host), created on first use
     int64_t hs_chunk = 0;                      // samples per channel of a staging slot
     float2 *hs_x[2] = {nullptr, nullptr};      // device input slots [nchan][hs_chunk]

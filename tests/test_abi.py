@@ -52,7 +52,7 @@ def test_status_strings(lib):
     (65, 64, 1, -1),        # M > N
     (5, 64, 0, -1),         # no channels
     (3, 4, 1, -2),          # N below the smallest kernel
-    (3, 1 << 17, 1, -2),    # N above the largest kernel
+    (3, 1 << 21, 1, -2),    # N above the largest kernel
 ])
 def test_plan_argument_checks(lib, M, N, nchan, status):
     with pytest.raises(fo.FirOlsError) as e:
