@@ -63,6 +63,10 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="calibrate FETCH_SIZE / WRITE_SIZE runs of this script against "
                          "the copy kernel, write profiles/ summaries, then exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="tabulate FETCH_SIZE / WRITE_SIZE per dispatch of every filtering "
+                         "kernel of a run with no copy kernel (e.g. tune_n.py), scaled by the "
+                         "calibration stored in profiles/traffic.json")
     ap.add_argument("--summarize-valu", metavar="DIR",
                     help="write profiles/ VALU summaries of a rocprofv3 --pmc run of this "
                          "script with the counters of VALU_COUNTERS, then exit")
@@ -82,6 +86,7 @@ def _csv_rows(d, suffix):
 
 
 def _short(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "")
     return name.split("(")[0].replace("void ", "")[:80]
 
 
@@ -93,7 +98,7 @@ def summarize_trace(args):
     out = os.path.join(PROFILES_DIR, f"{top}_{args.workload}_kernel_trace.md")
     lines = [f"# Kernel trace: {args.workload} ({WORKLOAD_NOTE.get(args.workload, '')})", "",
              "Command (working directory /tmp):", "", "```", args.command, "```", "",
-             f"Kernel source hash: `{kernel_source_hash()}`", "",
+             f"Kernel source hash: `{kernel_source_hash(args.workload)}`", "",
              "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
              "|---|---|---|---|---|---|"]
     for r in rows[:8]:
@@ -139,7 +144,8 @@ def summarize_pmc(args):
     except (OSError, ValueError):
         db = {}
     db[args.workload] = {"bytes_per_launch": round(per_launch), "algorithmic_bytes_per_launch": alg,
-                         "ratio": round(per_launch / alg, 4), "source_hash": kernel_source_hash(),
+                         "ratio": round(per_launch / alg, 4),
+                         "source_hash": kernel_source_hash(args.workload),
                          "fetch_scale": round(res["FETCH_SIZE"]["scale"], 4),
                          "write_scale": round(res["WRITE_SIZE"]["scale"], 4)}
     json.dump(db, open(path, "w"), indent=1, sort_keys=True)
@@ -148,7 +154,7 @@ def summarize_pmc(args):
     lines = [f"# HBM traffic: {args.workload} ({WORKLOAD_NOTE.get(args.workload, '')})", "",
              "Two counter runs of the same command, one per counter (working directory /tmp):",
              "", "```", args.command, "```", "",
-             f"Kernel source hash: `{kernel_source_hash()}`", "",
+             f"Kernel source hash: `{kernel_source_hash(args.workload)}`", "",
              "The counters are read per dispatch in KiB.  Each is scaled by the ratio of the true "
              "bytes to the counted KiB of the elementwise copy kernel in the same run "
              f"(`torch.neg` over {copy_kib:.0f} KiB read and written).", "",
@@ -164,6 +170,44 @@ def summarize_pmc(args):
                      f"{fb + wb:.4g} |")
     lines += ["", f"Algorithmic bytes per call (16 B per output sample): {alg:.4g}.  "
               f"Measured / algorithmic: {per_launch / alg:.3f}."]
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(out)
+
+
+def summarize_counters(args):
+    """profiles/<kernel>_<workload>_hbm_counters.md: per-dispatch HBM
+    counters of every filtering kernel, scaled by the counters' calibration
+    on the copy kernel of the bench runs (fetch_scale / write_scale of the
+    records in profiles/traffic.json)."""
+    db = json.load(open(os.path.join(PROFILES_DIR, "traffic.json")))
+    fs = float(np.median([r["fetch_scale"] for r in db.values()]))
+    ws = float(np.median([r["write_scale"] for r in db.values()]))
+    per = {}
+    for counter, d in (("FETCH_SIZE", args.summarize_counters[0]),
+                       ("WRITE_SIZE", args.summarize_counters[1])):
+        for r in _csv_rows(d, "counter_collection.csv"):
+            k = r["Kernel_Name"]
+            if r["Counter_Name"] == counter and "ols_" in k and "plan_taps" not in k:
+                per.setdefault(_short(k), {}).setdefault(counter, []).append(
+                    float(r["Counter_Value"]))
+    if not per:
+        raise SystemExit("no filtering kernel in the counter runs")
+    top = max(per, key=lambda k: np.mean(per[k].get("FETCH_SIZE", [0.0])))
+    top = top.split("::")[-1].replace("<", "_").replace(">", "")
+    out = os.path.join(PROFILES_DIR, f"{top}_{args.workload}_hbm_counters.md")
+    lines = [f"# HBM counters: {args.workload} ({WORKLOAD_NOTE.get(args.workload, '')})", "",
+             "Two counter runs of the same command, one per counter (working directory /tmp):",
+             "", "```", args.command, "```", "",
+             f"Kernel source hash: `{kernel_source_hash(args.workload)}`", "",
+             f"Mean KiB per dispatch; scaled bytes use FETCH_SIZE x {fs:.4g} and WRITE_SIZE x "
+             f"{ws:.4g}, the counters' calibration on an elementwise copy of known size.", "",
+             "| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled MB per dispatch |",
+             "|---|---|---|---|---|"]
+    for k in sorted(per):
+        f = float(np.mean(per[k].get("FETCH_SIZE", [0.0])))
+        w_ = float(np.mean(per[k].get("WRITE_SIZE", [0.0])))
+        lines.append(f"| `{k}` | {len(per[k].get('FETCH_SIZE', []))} | {f:.1f} | {w_:.1f} | "
+                     f"{(f * fs + w_ * ws) * 1024 / 1e6:.2f} |")
     open(out, "w").write("\n".join(lines) + "\n")
     print(out)
 
@@ -192,7 +236,7 @@ def summarize_valu(args):
     flops = 64.0 * (mean["SQ_INSTS_VALU_ADD_F32"] + mean["SQ_INSTS_VALU_MUL_F32"]
                     + 2.0 * mean["SQ_INSTS_VALU_FMA_F32"])
     samples = w.nchan * w.samples / len(w.calls)
-    rec = {"kernel": kern, "source_hash": kernel_source_hash(),
+    rec = {"kernel": kern, "source_hash": kernel_source_hash(args.workload),
            "valu_instr_per_launch": mean["SQ_INSTS_VALU"],
            "fp32_flops_per_launch": flops,
            "valu_instr_per_sample": round(64.0 * mean["SQ_INSTS_VALU"] / samples, 2),
@@ -209,7 +253,7 @@ def summarize_valu(args):
     out = os.path.join(PROFILES_DIR, f"{top}_{args.workload}_valu.md")
     lines = [f"# VALU counters: {args.workload} ({WORKLOAD_NOTE.get(args.workload, '')})", "",
              "One counter run (working directory /tmp):", "", "```", args.command, "```", "",
-             f"Kernel source hash: `{kernel_source_hash()}`", "",
+             f"Kernel source hash: `{kernel_source_hash(args.workload)}`", "",
              f"Mean per dispatch of `{kern}` ({len(per[kern]['SQ_WAVES'])} dispatches):", "",
              "| counter | value |", "|---|---|"]
     for c in names:
@@ -230,7 +274,7 @@ def measured_valu(workload: str):
         rec = json.load(open(path)).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if not rec or rec.get("source_hash") != kernel_source_hash(workload):
         return None
     return rec
 
@@ -286,21 +330,39 @@ def cpu_baseline(inp, seconds_budget: float = 20.0):
             "single_thread_sample": f"{n1} evenly spaced outputs of channel 0"}, ref
 
 
-# host-only sources: they launch the kernels but do not change what a kernel
-# reads, writes or executes
-HOST_ONLY_SOURCES = ("plan.cpp", "plan.hpp", "host_stream.cpp")
+# Device sources each filtering path is compiled from (its kernel file and
+# the headers that file includes); the counter records of a workload are
+# keyed by the hash of its path's sources, so a change to another path's
+# kernels leaves them valid.
+COMMON_DEVICE_SOURCES = ("kernels.hpp", "geometry.hpp", "dft.hpp", "ols_phases.hpp",
+                         "ols_block.hpp")
+PATH_SOURCES = {
+    "fused": ("ols_fused.hip",),
+    "big": ("ols_big.hip", "ols_big.hpp"),
+    "split": ("ols_split.hip", "ols_big.hpp"),
+    "multi": ("ols_multi.hip", "ols_big.hpp"),
+}
 
 
-def kernel_source_hash() -> str:
-    """Hash of the device-code sources (the .hip files and the headers they
-    include), which the counter records are keyed by."""
+def kernel_path(N: int) -> str:
+    """The filtering path of a plan with N-point blocks."""
+    return ("fused" if N <= 16384 else "big" if N == 32768 else "split" if N == 65536
+            else "multi")
+
+
+def kernel_source_hash(workload: str = "cfg2") -> str:
+    """Hash of the device sources of the workload's filtering path, which
+    its counter records are keyed by."""
     import hashlib
+
+    import workloads as W
+    w = W.WORKLOADS.get(workload)
+    path = kernel_path(w.N) if w is not None else "multi"
     d = os.path.join(ROOT, "order_fir_filtering_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".hpp", ".cpp", ".h")) and f not in HOST_ONLY_SOURCES:
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in sorted(PATH_SOURCES[path] + COMMON_DEVICE_SOURCES):
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -312,7 +374,7 @@ def measured_traffic(workload: str):
         rec = json.load(open(path)).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if not rec or rec.get("source_hash") != kernel_source_hash(workload):
         return None
     return rec.get("bytes_per_launch")
 
@@ -454,6 +516,7 @@ WORKLOAD_NOTE = {
     "cfg3": "M=8193, N=32768, 50331648 samples",
     "cfg4": "M=16385, N=65536 via H, 251658240 samples",
     "cfg5": "M=257, N=1024, 1024 channels x 65536 samples",
+    "n1048576": "M=262145, N=1048576, one call of 170 blocks (tune_n.py --logn 20 20)",
 }
 
 
@@ -470,6 +533,9 @@ def main():
         return
     if args.summarize_valu:
         summarize_valu(args)
+        return
+    if args.summarize_counters:
+        summarize_counters(args)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -633,7 +699,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(w.key),
             "avg_launch_us": round(kern_ms * 1e3, 3),
-            "kernel_source_hash": kernel_source_hash(),
+            "kernel_source_hash": kernel_source_hash(w.key),
             "algorithmic_bytes_per_launch": int(kern_bytes),
         },
         "valu": valu_line(w.key, kern_ms),

@@ -215,7 +215,7 @@ int fir_ols_destroy(fir_ols_plan_t p);
  * (N - M + 1) x blocks_per_second(N), from a table of block rates measured
  * on MI355X (one long single-channel call per N).  Returns N,
  * FIR_OLS_ERR_INVALID_ARG for M < 1, or FIR_OLS_ERR_UNSUPPORTED for
- * M > 65536.  Pure host arithmetic: no device call.
+ * M > 2^20.  Pure host arithmetic: no device call.
  */
 int64_t fir_ols_choose_n(int64_t M);
 

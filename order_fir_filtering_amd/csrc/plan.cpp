@@ -381,16 +381,18 @@ int fir_ols_destroy(fir_ols_plan_t p) {
 }
 
 int64_t fir_ols_choose_n(int64_t M) {
-    // blocks per second of N = 2^8 .. 2^16 on MI355X, measured by
+    // blocks per second of N = 2^8 .. 2^20 on MI355X, measured by
     // order_fir_filtering_amd/tune_n.py (one call of many blocks per N)
     static const double kBlocksPerSecond[] = {
-        1419658699.9, 711354696.3, 379209091.9,
-        173905752.5, 73544040.6, 21122692.5,
-        7899529.8, 7036289.6, 2221584.7};
+        1433645823.7, 699327776.7, 375217620.0,
+        174979853.7, 71174992.1, 21326771.6,
+        7920674.7, 6919868.1, 2237289.1,
+        769852.9, 370456.1, 189607.2,
+        91014.7};
     if (M < 1) return FIR_OLS_ERR_INVALID_ARG;
     int64_t best = FIR_OLS_ERR_UNSUPPORTED;
     double best_rate = 0.0;
-    for (int logn = 8; logn <= 16; ++logn) {
+    for (int logn = 8; logn <= firols::kMaxLogN; ++logn) {
         const int64_t N = (int64_t)1 << logn;
         if (N < M) continue;
         const double rate = (double)(N - M + 1) * kBlocksPerSecond[logn - 8];

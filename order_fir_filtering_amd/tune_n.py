@@ -1,13 +1,13 @@
 """Measure the filtering rate of every supported block size N on this GPU.
 
-For each N = 2^8 .. 2^16 the script times one long single-channel call with
+For each N = 2^8 .. 2^20 the script times one long single-channel call with
 M = N/4 + 1 (so L = 3N/4) and many blocks, and records blocks per second.
 A block's cost depends on N, not on M (the transform is the same; only the
 number of kept outputs changes), so the output rate of a plan (M, N) is
 about (N - M + 1) x blocks_per_second(N): the planner choice of N for a
 given M (the method page leaves N free, claim 1 step 1) maximizes that.
 
-    python -m order_fir_filtering_amd.tune_n [--out FILE]
+    python -m order_fir_filtering_amd.tune_n [--out FILE] [--logn LO HI]
 
 prints one JSON object {N: blocks_per_second} (and writes it to FILE).
 """
@@ -20,29 +20,26 @@ import sys
 import numpy as np
 
 
-def sweep(max_samples: int = 1 << 27) -> dict:
+def sweep(max_samples: int = 1 << 27, lo: int = 8, hi: int = 20) -> dict:
     import torch
 
     import order_fir_filtering_amd as fo
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(11)
     res = {}
-    for logn in range(8, 17):
+    for logn in range(lo, hi + 1):
         N = 1 << logn
         M = N // 4 + 1
         L = N - M + 1
-        nblk = max(1024, min(max_samples // L, 1 << 20))
+        # enough blocks to fill the GPU: one block per workgroup up to
+        # N = 65536, while a larger block spreads over many workgroups
+        nblk = max(1024 if logn <= 16 else 64, min(max_samples // L, 1 << 20))
         n = nblk * L
         x = torch.randn(n, dtype=torch.complex64, device=dev)
         y = torch.empty_like(x)
         h = (rng.standard_normal(M) / np.sqrt(M)).astype(np.float32)
         with fo.Plan(M, N, 1) as p:
-            if N == 65536:
-                hp = np.zeros(N, np.complex128)
-                hp[:M] = h
-                p.set_freq_response(np.fft.fft(hp).astype(np.complex64))
-            else:
-                p.set_taps(h)
+            p.set_taps(h)
             for _ in range(3):
                 p.execute(x, y)
             torch.cuda.synchronize()
@@ -65,8 +62,10 @@ def sweep(max_samples: int = 1 << 27) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default="")
+    ap.add_argument("--logn", type=int, nargs=2, default=(8, 20), metavar=("LO", "HI"),
+                    help="sweep N = 2^LO .. 2^HI only")
     a = ap.parse_args()
-    res = sweep()
+    res = sweep(lo=a.logn[0], hi=a.logn[1])
     text = json.dumps({str(k): round(v, 1) for k, v in res.items()})
     print(text)
     if a.out:

@@ -67,7 +67,7 @@ def test_valu_summary_and_line(tmp_path, monkeypatch):
     samples = w.nchan * w.samples / len(w.calls)
     assert rec["fp32_flops_per_sample"] == pytest.approx(want / samples, abs=0.01)
     assert rec["valu_instr_per_sample"] == pytest.approx(64 * instr / samples, abs=0.01)
-    assert rec["source_hash"] == bench.kernel_source_hash()
+    assert rec["source_hash"] == bench.kernel_source_hash("cfg2")
     assert (prof / "ols_fused_kernel_12_cfg2_valu.md").exists()
 
     monkeypatch.setattr(bench, "PROFILES_DIR", str(prof))

@@ -22,7 +22,8 @@ def best(M):
 
 def test_choice_maximizes_the_measured_rate():
     for M in list(range(1, 300)) + [511, 512, 513, 1025, 2049, 4097, 8193, 16384, 16385,
-                                    32768, 40000, 65536]:
+                                    32768, 40000, 65536, 65537, 100000, 131073, 200000,
+                                    262145, 500000, 524289, 1 << 20]:
         want = best(M)
         if want is None:
             with pytest.raises(fo.FirOlsError) as e:
@@ -38,7 +39,7 @@ def test_choice_arguments():
     with pytest.raises(fo.FirOlsError) as e:
         fo.fir_ols_choose_n(0)
     assert e.value.status == -1
-    assert fo.fir_ols_choose_n(65536) == 65536
+    assert fo.fir_ols_choose_n(1 << 20) == 1 << 20
     with pytest.raises(fo.FirOlsError) as e:
-        fo.fir_ols_choose_n(65537)
+        fo.fir_ols_choose_n((1 << 20) + 1)
     assert e.value.status == -2
