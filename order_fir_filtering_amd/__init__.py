@@ -25,15 +25,17 @@ __all__ = [
     "fir_ols_plan", "fir_ols_set_taps", "fir_ols_set_freq_response",
     "fir_ols_execute", "fir_ols_execute_host", "fir_ols_execute_real", "fir_ols_set_state",
     "fir_ols_get_state", "fir_ols_destroy", "fir_ols_block_length", "fir_ols_choose_n",
-    "fir_ols_status_string",
+    "fir_ols_status_string", "Channelizer", "fir_pfb_plan", "fir_pfb_set_taps",
+    "fir_pfb_execute", "fir_pfb_set_state", "fir_pfb_get_state", "fir_pfb_destroy",
 ]
 
-# Every symbol include/firols.h declares.
+# Every symbol include/firols.h and include/firpfb.h declare.
 EXPORTED = (
     "fir_ols_plan", "fir_ols_set_taps", "fir_ols_set_freq_response",
     "fir_ols_execute", "fir_ols_execute_host", "fir_ols_execute_real", "fir_ols_set_state",
     "fir_ols_get_state", "fir_ols_destroy", "fir_ols_block_length", "fir_ols_choose_n",
-    "fir_ols_status_string",
+    "fir_ols_status_string", "fir_pfb_plan", "fir_pfb_set_taps", "fir_pfb_execute",
+    "fir_pfb_set_state", "fir_pfb_get_state", "fir_pfb_destroy",
 )
 
 STATUS = {
@@ -79,6 +81,12 @@ def load_library(path: Optional[str] = None):
         "fir_ols_block_length": (_i64, [_vp]),
         "fir_ols_choose_n": (_i64, [_i64]),
         "fir_ols_status_string": (ctypes.c_char_p, [_int]),
+        "fir_pfb_plan": (_int, [ctypes.POINTER(_vp), _i64, _i64, _i64]),
+        "fir_pfb_set_taps": (_int, [_vp, _vp, _i64, _vp]),
+        "fir_pfb_execute": (_int, [_vp, _vp, _vp, _i64, _vp]),
+        "fir_pfb_set_state": (_int, [_vp, _vp, _i64, _vp]),
+        "fir_pfb_get_state": (_int, [_vp, _vp, ctypes.POINTER(_i64), _vp]),
+        "fir_pfb_destroy": (_int, [_vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -275,6 +283,100 @@ class Plan:
     def close(self) -> None:
         if getattr(self, "handle", None):
             fir_ols_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+# Polyphase filter-bank channelizer (include/firpfb.h).
+
+def fir_pfb_plan(K: int, D: int, Nh: int) -> int:
+    """Create a channelizer plan; returns the opaque handle as an integer."""
+    lib = load_library()
+    h = _vp()
+    _check(lib.fir_pfb_plan(ctypes.byref(h), K, D, Nh), "fir_pfb_plan")
+    return h.value
+
+
+def fir_pfb_set_taps(plan: int, h, stream=None) -> None:
+    """Real prototype taps from host memory (float32, length Nh)."""
+    lib = load_library()
+    arr = np.ascontiguousarray(np.asarray(h), dtype=np.float32)
+    _check(lib.fir_pfb_set_taps(plan, arr.ctypes.data, arr.size, _stream(stream)),
+           "fir_pfb_set_taps")
+
+
+def fir_pfb_execute(plan: int, x, y, nsamples: int, stream=None) -> None:
+    _check(load_library().fir_pfb_execute(plan, _ptr(x), _ptr(y), nsamples, _stream(stream)),
+           "fir_pfb_execute")
+
+
+def fir_pfb_set_state(plan: int, s=None, t_next: int = 0, stream=None) -> None:
+    _check(load_library().fir_pfb_set_state(plan, _ptr(s), t_next, _stream(stream)),
+           "fir_pfb_set_state")
+
+
+def fir_pfb_get_state(plan: int, out=None, stream=None) -> int:
+    """Copies the state to out (if given); returns the next stream time."""
+    t = _i64(0)
+    _check(load_library().fir_pfb_get_state(plan, _ptr(out), ctypes.byref(t), _stream(stream)),
+           "fir_pfb_get_state")
+    return int(t.value)
+
+
+def fir_pfb_destroy(plan: Optional[int]) -> None:
+    if plan:
+        _check(load_library().fir_pfb_destroy(plan), "fir_pfb_destroy")
+
+
+class Channelizer:
+    """Owning wrapper of a channelizer plan on torch complex64 device tensors."""
+
+    def __init__(self, K: int, D: int, Nh: int):
+        self.K, self.D, self.Nh = int(K), int(D), int(Nh)
+        self.handle = fir_pfb_plan(self.K, self.D, self.Nh)
+
+    def set_taps(self, h, stream=None) -> "Channelizer":
+        fir_pfb_set_taps(self.handle, h, stream)
+        return self
+
+    def execute(self, x, y=None, stream=None):
+        """Channelize x (complex64 [n], n a multiple of D); returns y [n / D, K]."""
+        import torch
+        if x.dtype != torch.complex64 or not x.is_cuda or x.dim() != 1 or (
+                x.shape[0] > 1 and x.stride(0) != 1):
+            raise FirOlsError(-1, "execute: x must be a contiguous complex64 device vector")
+        n = x.shape[0]
+        if y is None:
+            y = torch.empty((n // self.D, self.K), dtype=x.dtype, device=x.device)
+        elif y.shape != (n // self.D, self.K) or not y.is_contiguous() or y.dtype != x.dtype:
+            raise FirOlsError(-1, "execute: y must be a contiguous [n / D, K] complex64 tensor")
+        fir_pfb_execute(self.handle, x, y, n, stream)
+        return y
+
+    def set_state(self, s=None, t_next: int = 0, stream=None) -> None:
+        fir_pfb_set_state(self.handle, s, t_next, stream)
+
+    def get_state(self, stream=None):
+        """(state tensor [Nh - 1], next stream time)."""
+        import torch
+        out = torch.empty((max(self.Nh - 1, 1),), dtype=torch.complex64, device="cuda")
+        t = fir_pfb_get_state(self.handle, out, stream)
+        return out[:self.Nh - 1], t
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            fir_pfb_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

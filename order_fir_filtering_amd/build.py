@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfirols.so")
 SOURCES = ["plan.cpp", "host_stream.cpp", "ols_fused.hip", "ols_big.hip", "ols_split.hip",
-           "ols_multi.hip"]
+           "ols_multi.hip", "pfb_plan.cpp", "pfb.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

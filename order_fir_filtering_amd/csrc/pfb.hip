@@ -1,0 +1,231 @@
+// Polyphase filter-bank channelizer (the channelizer page, "GPU polyphase
+// filter bank channelizer", sections 2.1 and 2.2) on the overlap-save
+// library's register/LDS FFT.
+//
+// Channel c of output m is the stream shifted to baseband, filtered by the
+// real prototype h (Nh taps) and decimated by D:
+//   y_c(m) = sum_p h(p) xt(t_m - p) W^{c (t_m - p)},  W = exp(-2 pi j / K),
+// t_m the time of the last sample of output m's hop.  With p = n K + k
+// (the page's polyphase split, h_k(n) = h(n K + k)) and W^{-c n K} = 1:
+//   y_c(m) = W^{c t_m} sum_k W^{-c k} v_k(m),
+//   v_k(m) = sum_n h(n K + k) xt(t_m - n K - k),
+// i.e. the branch filters of section 2.1, a K-point DFT across the
+// branches (its bin -c mod K for channel c), and the baseband phase
+// W^{c t_m}.  A workgroup takes a tile of TM consecutive outputs: it loads
+// the tile's input span (T K + (TM - 1) D samples) into LDS once, then each
+// group of K / 16 threads (one K-point transform, 16 points per thread)
+// forms the K branch sums of one output from LDS with its taps held in
+// registers, transforms them, reorders the bins through LDS into channel
+// order and stores the row of K channels.
+#include "pfb.hpp"
+
+#include "ols_block.hpp"
+
+namespace firpfb {
+
+using firols::ic;
+using firols::static_for;
+
+namespace {
+
+constexpr int kThreads = 256;
+// LDS of one workgroup: the transforms' exchange areas, then the input span
+constexpr int kWinMax = 14336;
+
+template <int LOGK>
+struct PfbGeo {
+    static constexpr int gid = firols::geo_id(LOGK);
+    static constexpr firols::Geo G = firols::make_geo(gid);
+    static constexpr int K = G.N;
+    static constexpr int TB = G.TB;                 // threads per transform
+    static constexpr int FPW = kThreads / TB;       // transforms per workgroup at once
+    static constexpr int FFT_LDS = FPW * G.lds_stride;
+    static_assert(G.P == 16 && TB <= 64, "one transform inside one wave");
+};
+
+// Bin held by register r of thread tb after the forward passes.
+template <int LOGK>
+__device__ __forceinline__ int bin_of_register(int tb, int r) {
+    constexpr firols::Geo G = PfbGeo<LOGK>::G;
+    return firols::bin_of_position(G, firols::last_pass_position(G, tb, r));
+}
+
+template <int LOGK, int T>
+__global__ __launch_bounds__(kThreads) void pfb_kernel(PfbArgs A) {
+    using PG = PfbGeo<LOGK>;
+    constexpr firols::Geo G = PG::G;
+    constexpr int K = PG::K, TB = PG::TB;
+    __shared__ float2 smem[PG::FFT_LDS + kWinMax];
+    const int grp = threadIdx.x / TB;
+    const int tb = threadIdx.x - grp * TB;
+    float2 *fl = smem + grp * G.lds_stride;
+    float2 *win = smem + PG::FFT_LDS;
+
+    // this thread's taps: register r holds branch k = tb + TB pass0_m(r)
+    float hr[T][16];
+    static_for<0, T>([&](auto Nn) {
+        constexpr int n = decltype(Nn)::value;
+        static_for<0, 16>([&](auto Rr) {
+            constexpr int r = decltype(Rr)::value;
+            hr[n][r] = A.taps[n * K + tb + TB * firols::pass0_m<PG::gid>(r)];
+        });
+    });
+    const firols::TwTable<PG::gid> tw{A.tw, tb};
+    const int Nm1 = A.Nh - 1;
+    const int span = T * K + (A.TM - 1) * A.D;
+    const int64_t tiles = (A.nout + A.TM - 1) / A.TM;
+
+    for (int64_t it = 0;; ++it) {
+        const int64_t tile = firols::unit_of(tiles, blockIdx.x, gridDim.x, it);
+        if (tile < 0) break;
+        const int64_t m0 = tile * A.TM;
+        // input span of the tile: times (relative to x[0]) from w0 on
+        const int64_t w0 = m0 * A.D + A.D - T * K;
+        __syncthreads();                      // the previous tile's span is no longer read
+        for (int e = threadIdx.x; e < span; e += kThreads) {
+            const int64_t g = w0 + e;
+            float2 v = make_float2(0.f, 0.f);
+            if (g >= 0) {
+                if (g < A.nsamples) v = A.x[g];
+            } else if (g >= -(int64_t)Nm1) {
+                v = A.s_old[Nm1 + g];
+            }
+            win[e] = v;
+        }
+        __syncthreads();
+
+        for (int j = grp; j < A.TM; j += PG::FPW) {
+            const int64_t m = m0 + j;
+            // branch sums; the sample of tap n of branch k is at span index
+            // j D + T K - 1 - n K - k
+            const int base = j * A.D + T * K - 1 - tb;
+            float2 a[16];
+            static_for<0, 16>([&](auto Rr) {
+                constexpr int r = decltype(Rr)::value;
+                constexpr int kk = TB * firols::pass0_m<PG::gid>(r);
+                float2 s = make_float2(0.f, 0.f);
+                static_for<0, T>([&](auto Nn) {
+                    constexpr int n = decltype(Nn)::value;
+                    const float2 v = win[base - n * K - kk];
+                    s.x = fmaf(hr[n][r], v.x, s.x);
+                    s.y = fmaf(hr[n][r], v.y, s.y);
+                });
+                a[r] = s;
+            });
+            firols::forward_all<PG::gid>(tb, a, fl, tw);
+            // bins to channel order: bin b is channel (K - b) mod K
+            firols::wave_sync();
+            static_for<0, 16>([&](auto Rr) {
+                constexpr int r = decltype(Rr)::value;
+                const int c = (K - bin_of_register<LOGK>(tb, r)) & (K - 1);
+                fl[firols::lds_pad(G, c)] = a[r];
+            });
+            firols::wave_sync();
+            // baseband phase W^{c t_m}, t_m = t0 + m D + D - 1 (mod K)
+            const int tm = (int)((A.t0 + (m % K) * A.D + A.D - 1) & (K - 1));
+            if (m < A.nout) {
+                float2 *yr = A.y + m * K;
+                static_for<0, 16>([&](auto Jj) {
+                    constexpr int jj = decltype(Jj)::value;
+                    const int c = tb + TB * jj;
+                    const float2 v = fl[firols::lds_pad(G, c)];
+                    const float2 w = A.phase[(c * tm) & (K - 1)];
+                    __builtin_nontemporal_store(v.x * w.x - v.y * w.y, &yr[c].x);
+                    __builtin_nontemporal_store(v.x * w.y + v.y * w.x, &yr[c].y);
+                });
+            }
+            firols::wave_sync();          // the exchange area is reused by the next output
+        }
+    }
+}
+
+// The last Nh - 1 samples of {s_old, x}.
+__global__ void pfb_state_kernel(const float2 *__restrict__ x, int64_t n,
+                                 const float2 *__restrict__ s_old, float2 *__restrict__ s_new,
+                                 int Nm1) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= Nm1) return;
+    const int64_t g = n - Nm1 + i;
+    s_new[i] = g >= 0 ? x[g] : s_old[Nm1 + g];
+}
+
+template <int LOGK, int T>
+const void *kernel_ptr() {
+    return reinterpret_cast<const void *>(&pfb_kernel<LOGK, T>);
+}
+
+template <int LOGK>
+hipError_t launch_k(const PfbArgs &a, int T, dim3 grid, hipStream_t s) {
+    if (T == 2) hipLaunchKernelGGL((pfb_kernel<LOGK, 2>), grid, dim3(kThreads), 0, s, a);
+    else if (T == 4) hipLaunchKernelGGL((pfb_kernel<LOGK, 4>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((pfb_kernel<LOGK, 8>), grid, dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int LOGK>
+const void *kernel_of(int T) {
+    return T == 2 ? kernel_ptr<LOGK, 2>() : T == 4 ? kernel_ptr<LOGK, 4>() : kernel_ptr<LOGK, 8>();
+}
+
+int log2_of(int K) {
+    int l = 0;
+    while ((1 << l) < K) ++l;
+    return l;
+}
+
+}  // namespace
+
+int taps_per_branch(int K, int Nh) {
+    const int t = (Nh + K - 1) / K;
+    return t <= 2 ? 2 : t <= 4 ? 4 : t <= 8 ? 8 : 0;
+}
+
+int tile_outputs(int K, int D, int T) {
+    const int fpw = kThreads / (K / 16);
+    if (T * K + (fpw - 1) * D > kWinMax) return 0;
+    int tm = (kWinMax - T * K) / D + 1;      // T K + (tm - 1) D <= kWinMax
+    tm -= tm % fpw;
+    return tm > 8 * fpw ? 8 * fpw : tm;
+}
+
+int twiddle_count(int K) { return firols::twiddle_count(firols::geo_id(log2_of(K))); }
+
+void build_twiddles(int K, float2 *out) { firols::build_twiddles(firols::geo_id(log2_of(K)), out); }
+
+int max_groups(int K, int T, int device) {
+    const int lk = log2_of(K);
+    const void *f = lk == 6 ? kernel_of<6>(T) : lk == 7 ? kernel_of<7>(T) : lk == 8 ? kernel_of<8>(T)
+                    : lk == 9 ? kernel_of<9>(T) : kernel_of<10>(T);
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+        cus < 1)
+        cus = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kThreads, 0) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    return cus * per_cu;
+}
+
+hipError_t launch(const PfbArgs &a, int T, int max_groups, hipStream_t s) {
+    const int lk = log2_of(a.K);
+    if (a.nout <= 0 || a.TM <= 0 || (1 << lk) != a.K || lk < kMinLogK || lk > kMaxLogK ||
+        (T != 2 && T != 4 && T != 8))
+        return hipErrorInvalidConfiguration;
+    const int64_t tiles = (a.nout + a.TM - 1) / a.TM;
+    int64_t grid = tiles;
+    if (grid > max_groups) grid = max_groups & ~7;    // persistent, multiple of 8
+    if (grid <= 0) grid = tiles < max_groups ? tiles : max_groups;
+    const dim3 g((unsigned)grid);
+    hipError_t e = lk == 6   ? launch_k<6>(a, T, g, s)
+                   : lk == 7 ? launch_k<7>(a, T, g, s)
+                   : lk == 8 ? launch_k<8>(a, T, g, s)
+                   : lk == 9 ? launch_k<9>(a, T, g, s)
+                             : launch_k<10>(a, T, g, s);
+    if (e != hipSuccess || a.Nh <= 1) return e;
+    const int nm1 = a.Nh - 1;
+    hipLaunchKernelGGL(pfb_state_kernel, dim3((unsigned)((nm1 + 255) / 256)), dim3(256), 0, s,
+                       a.x, a.nsamples, a.s_old, a.s_new, nm1);
+    return hipGetLastError();
+}
+
+}  // namespace firpfb

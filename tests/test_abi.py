@@ -1,4 +1,4 @@
-"""The C ABI library loads and exports what include/firols.h declares (CPU).
+"""The C ABI library loads and exports what include/*.h declare (CPU).
 
 Only argument checks that return before any HIP call are exercised here.
 """
@@ -10,13 +10,21 @@ import pytest
 import order_fir_filtering_amd as fo
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "firols.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("firols.h", "firpfb.h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fir_ols_\w+)\s*\(", text)))
+    names = set()
+    for hdr in HEADERS:
+        text = open(hdr).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(fir_(?:ols|pfb)_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_headers_are_all_listed():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == sorted(
+        os.path.basename(h) for h in HEADERS)
 
 
 @pytest.fixture(scope="module")
@@ -74,3 +82,27 @@ def test_null_handles(lib):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(fo.FirOlsError):
         fo.load_library(str(tmp_path / "libfirols.so"))
+
+
+@pytest.mark.parametrize("K,D,Nh,status", [
+    (100, 50, 10, -1),       # K not a power of two
+    (128, 48, 10, -1),       # D does not divide K
+    (128, 256, 10, -1),      # D above K
+    (128, 64, 0, -1),        # no taps
+    (32, 16, 10, -2),        # K below the smallest transform
+    (2048, 1024, 10, -2),    # K above the largest transform
+    (128, 64, 8 * 128 + 1, -2),   # more than 8 taps per branch
+])
+def test_channelizer_plan_argument_checks(lib, K, D, Nh, status):
+    with pytest.raises(fo.FirOlsError) as e:
+        fo.fir_pfb_plan(K, D, Nh)
+    assert e.value.status == status
+
+
+def test_channelizer_null_handles(lib):
+    assert lib.fir_pfb_destroy(None) == 0
+    assert lib.fir_pfb_execute(None, None, None, 64, None) == -1
+    assert lib.fir_pfb_set_taps(None, None, 3, None) == -1
+    assert lib.fir_pfb_set_state(None, None, 0, None) == -1
+    assert lib.fir_pfb_get_state(None, None, None, None) == -1
+    assert lib.fir_pfb_plan(None, 128, 64, 10) == -1
