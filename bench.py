@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=-1,
                     help="untimed warm-up steps (default: about one second of steps)")
     ap.add_argument("--workload", default="cfg2",
-                    help="cfg1..cfg5 (default cfg2: M=1025, N=4096, 4 calls)")
+                    help="cfg1..cfg5 (default cfg2: M=1025, N=4096, 4 calls), or a "
+                         "channelizer workload (pfb1024, pfb128) measured alone")
     ap.add_argument("--host-stream", action="store_true",
                     help="also time the host-resident streaming call (pinned host input "
                          "and output, copies overlapped with filtering); adds host_stream")
@@ -55,6 +56,9 @@ def parse():
     ap.add_argument("--real", action="store_true",
                     help="also time real-valued input (two real rows per channel of the "
                          "workload, 8 B per real sample); adds real_pairs")
+    ap.add_argument("--channelizer", default="", metavar="WORKLOAD",
+                    help="also measure the polyphase channelizer on this workload "
+                         "(pfb1024 or pfb128): adds a 'channelizer' object to the line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -493,6 +497,76 @@ def real_pairs(inp, fo, torch, stream, nsets):
             "rows": 2 * w.nchan, "samples_per_row": w.samples}
 
 
+def channelizer(args, fo, torch, stream):
+    """The polyphase channelizer on one of its workloads: parity of one call
+    against the oracle on sampled output rows, then K timed calls of the
+    whole input (the state and stream time carry from call to call), the
+    per-launch rate against the HBM roof (8 B read per input sample, K/D
+    outputs of 8 B written per hop of D samples), and the oracle timed on a
+    bounded sample of rows."""
+    import oracle
+    import workloads as W
+    key = args.channelizer
+    w = W.PFB_WORKLOADS[key]
+    K, D, Nh, n = w["K"], w["D"], w["Nh"], w["samples"]
+    h, x_host = W.make_pfb_inputs(key)
+    x = torch.from_numpy(x_host).to("cuda:0")
+    y = torch.empty((n // D, K), dtype=torch.complex64, device="cuda:0")
+    c = fo.Channelizer(K, D, Nh)
+    c.set_taps(h)
+    sptr = stream.cuda_stream
+    out = {"workload": f"{key}: {w['description']}", "K": K, "D": D, "Nh": Nh,
+           "samples_per_call": n, "outputs_per_call": n // D * K}
+    # parity: the first call from zero state and time 0, sampled rows
+    fo.fir_pfb_execute(c.handle, x, y, n, sptr)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(16), W.sample_indices(11, n // D, 48),
+                                     [n // D - 1]]))
+    yg = y.cpu().numpy()[rows]
+    ref = oracle.pfb_channelize(h, x_host, K, D, idx=rows)
+    err = float(np.abs(yg.astype(np.complex128) - ref).max())
+    bound = oracle.pfb_parity_bound(h, x_host)
+    out["parity"] = {"max_abs_err": err, "bound": bound, "ok": err <= bound,
+                     "rows_checked": int(rows.size), "outputs_checked": int(ref.size)}
+    for _ in range(5):
+        fo.fir_pfb_execute(c.handle, x, y, n, sptr)
+    steps = max(10, args.steps if args.steps > 0 else 20)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fo.fir_pfb_execute(c.handle, x, y, n, sptr)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    c.close()
+    byts = n * 8 + (n // D) * K * 8
+    gbps = byts / (ms * 1e-3) / 1e9
+    out.update({"metric": "channelized input Msamples/s (complex fp32)", "unit": "Msamples/s",
+                "value": round(n / (ms * 1e-3) / 1e6, 1), "ms_per_call": round(ms, 4),
+                "steps": steps,
+                "roofline": {"bound": "hbm", "kernel": f"pfb_kernel<{int(np.log2(K))}, 8>",
+                             "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                             "algorithmic_bytes_per_launch": int(byts),
+                             "bytes_per_input_sample": 8 + 8 * K / D}})
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):            # one core, BLAS included
+            t0 = time.perf_counter()
+            oracle.pfb_channelize(h, x_host, K, D, idx=np.arange(8))
+            per = (time.perf_counter() - t0) / 8
+            nrow = int(max(8, min(n // D, 15.0 / max(per, 1e-9))))
+            t0 = time.perf_counter()
+            oracle.pfb_channelize(h, x_host, K, D, idx=np.arange(nrow))
+            sec = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(nrow * D / sec / 1e6, 4), "unit": "Msamples/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"first {nrow} output rows ({nrow * D} input "
+                                         "samples), float64, one thread"}
+    return out
+
+
 def valu_line(workload: str, kern_ms: float):
     """fp32 VALU throughput of the filtering kernel: counted flops per
     launch (committed counter run of the same sources) over the live
@@ -551,6 +625,24 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     fo.load_library()
+
+    if args.workload in W.PFB_WORKLOADS:
+        # the channelizer alone: its own line, same contract fields
+        args.channelizer = args.workload
+        wall0 = time.perf_counter()
+        ch = channelizer(args, fo, torch, torch.cuda.current_stream())
+        line = {"metric": ch.pop("metric"), "value": ch.pop("value"), "unit": ch.pop("unit"),
+                "n_gpus": 1, "steps": ch.pop("steps"), "warmup": 5,
+                "ms_per_step": ch.pop("ms_per_call"), "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+                "config": {"workload": ch.pop("workload"), "K": ch.pop("K"), "D": ch.pop("D"),
+                           "Nh": ch.pop("Nh"), "samples_per_step": ch.pop("samples_per_call"),
+                           "outputs_per_step": ch.pop("outputs_per_call")},
+                "roofline": ch.pop("roofline"), "parity": ch.pop("parity"),
+                "cpu_baseline": ch.pop("cpu_baseline", None),
+                "wall_s": round(time.perf_counter() - wall0, 3)}
+        print(json.dumps(line), flush=True)
+        return
 
     inp = W.make_inputs(args.workload)
     w = inp.workload
@@ -669,6 +761,7 @@ def main():
     plan.close()
     host = host_stream(args, inp, fo, torch, stream) if args.host_stream else None
     real = real_pairs(inp, fo, torch, stream, nsets) if args.real else None
+    chan = channelizer(args, fo, torch, stream) if args.channelizer else None
     out = {
         "metric": "filtered output Msamples/s (complex fp32) and % of HBM roof, per (M,N)",
         "value": round(value, 1),
@@ -706,6 +799,7 @@ def main():
         "copy_reference_GBps": round(copy_gbps, 1),
         "host_stream": host,
         "real_pairs": real,
+        "channelizer": chan,
         "parity": parity,
         "cpu_baseline": base,
         "wall_s": round(wall, 3),

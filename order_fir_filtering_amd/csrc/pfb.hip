@@ -16,7 +16,8 @@
 // group of K / 16 threads (one K-point transform, 16 points per thread)
 // forms the K branch sums of one output from LDS with its taps held in
 // registers, transforms them, reorders the bins through LDS into channel
-// order and stores the row of K channels.
+// order, applies the baseband phase (t_m = t0 + m D + D - 1 mod K) and
+// stores the row of K channels.
 #include "pfb.hpp"
 
 #include "ols_block.hpp"
@@ -31,6 +32,9 @@ namespace {
 constexpr int kThreads = 256;
 // LDS of one workgroup: the transforms' exchange areas, then the input span
 constexpr int kWinMax = 14336;
+constexpr int kFill = 16;          // input loads in flight per thread while filling LDS
+// two floats as a clang vector, for the non-temporal store builtin
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <int LOGK>
 struct PfbGeo {
@@ -70,7 +74,10 @@ __global__ __launch_bounds__(kThreads) void pfb_kernel(PfbArgs A) {
             hr[n][r] = A.taps[n * K + tb + TB * firols::pass0_m<PG::gid>(r)];
         });
     });
-    const firols::TwTable<PG::gid> tw{A.tw, tb};
+    // the transform's twiddles in registers, loaded once (a table read per
+    // pass would expose its latency to every output: one wave per SIMD)
+    firols::TwRegs<PG::gid> tw;
+    tw.load(A.tw, tb);
     const int Nm1 = A.Nh - 1;
     const int span = T * K + (A.TM - 1) * A.D;
     const int64_t tiles = (A.nout + A.TM - 1) / A.TM;
@@ -82,15 +89,36 @@ __global__ __launch_bounds__(kThreads) void pfb_kernel(PfbArgs A) {
         // input span of the tile: times (relative to x[0]) from w0 on
         const int64_t w0 = m0 * A.D + A.D - T * K;
         __syncthreads();                      // the previous tile's span is no longer read
-        for (int e = threadIdx.x; e < span; e += kThreads) {
-            const int64_t g = w0 + e;
-            float2 v = make_float2(0.f, 0.f);
-            if (g >= 0) {
-                if (g < A.nsamples) v = A.x[g];
-            } else if (g >= -(int64_t)Nm1) {
-                v = A.s_old[Nm1 + g];
+        // kFill loads per thread are requested before the first is written
+        // to LDS, so their latencies overlap
+        const bool inside = w0 >= 0 && w0 + span <= A.nsamples;
+        for (int e0 = threadIdx.x; e0 < span; e0 += kThreads * kFill) {
+            float2 v[kFill];
+            if (inside) {
+                const float2 *__restrict__ xs = A.x + w0;
+                static_for<0, kFill>([&](auto Bb) {
+                    constexpr int b = decltype(Bb)::value;
+                    const int e = e0 + b * kThreads;
+                    v[b] = e < span ? xs[e] : make_float2(0.f, 0.f);
+                });
+            } else {
+                static_for<0, kFill>([&](auto Bb) {
+                    constexpr int b = decltype(Bb)::value;
+                    const int64_t g = w0 + e0 + b * kThreads;
+                    float2 u = make_float2(0.f, 0.f);
+                    if (g >= 0) {
+                        if (g < A.nsamples && e0 + b * kThreads < span) u = A.x[g];
+                    } else if (g >= -(int64_t)Nm1) {
+                        u = A.s_old[Nm1 + g];
+                    }
+                    v[b] = u;
+                });
             }
-            win[e] = v;
+            static_for<0, kFill>([&](auto Bb) {
+                constexpr int b = decltype(Bb)::value;
+                const int e = e0 + b * kThreads;
+                if (e < span) win[e] = v[b];
+            });
         }
         __syncthreads();
 
@@ -112,6 +140,14 @@ __global__ __launch_bounds__(kThreads) void pfb_kernel(PfbArgs A) {
                 });
                 a[r] = s;
             });
+            // the baseband phases W^{c t_m} of this thread's channels, requested
+            // before the transform so their latency overlaps it
+            const int tm = (int)((A.t0 + (m % K) * A.D + A.D - 1) & (K - 1));
+            float2 w[16];
+            static_for<0, 16>([&](auto Jj) {
+                constexpr int jj = decltype(Jj)::value;
+                w[jj] = A.phase[((tb + TB * jj) * tm) & (K - 1)];
+            });
             firols::forward_all<PG::gid>(tb, a, fl, tw);
             // bins to channel order: bin b is channel (K - b) mod K
             firols::wave_sync();
@@ -121,17 +157,14 @@ __global__ __launch_bounds__(kThreads) void pfb_kernel(PfbArgs A) {
                 fl[firols::lds_pad(G, c)] = a[r];
             });
             firols::wave_sync();
-            // baseband phase W^{c t_m}, t_m = t0 + m D + D - 1 (mod K)
-            const int tm = (int)((A.t0 + (m % K) * A.D + A.D - 1) & (K - 1));
             if (m < A.nout) {
                 float2 *yr = A.y + m * K;
                 static_for<0, 16>([&](auto Jj) {
                     constexpr int jj = decltype(Jj)::value;
                     const int c = tb + TB * jj;
                     const float2 v = fl[firols::lds_pad(G, c)];
-                    const float2 w = A.phase[(c * tm) & (K - 1)];
-                    __builtin_nontemporal_store(v.x * w.x - v.y * w.y, &yr[c].x);
-                    __builtin_nontemporal_store(v.x * w.y + v.y * w.x, &yr[c].y);
+                    const f32x2 o = {v.x * w[jj].x - v.y * w[jj].y, v.x * w[jj].y + v.y * w[jj].x};
+                    __builtin_nontemporal_store(o, (f32x2 *)(yr + c));
                 });
             }
             firols::wave_sync();          // the exchange area is reused by the next output

@@ -172,3 +172,28 @@ def sample_indices(seed: int, total: int, count: int) -> np.ndarray:
     rng = np.random.default_rng(seed)
     count = min(count, total)
     return np.sort(rng.choice(total, size=count, replace=False)).astype(np.int64)
+
+
+# Channelizer workloads (the polyphase-channelizer page, "GPU polyphase
+# filter bank channelizer": section 2.2's 50 % overlap, D = K / 2, for its
+# 1024- and 128-channel configurations).  The prototype is the page's
+# window-method low-pass, cutoff 1/D of Nyquist with a Hamming window, here
+# 8 taps per branch; the input is complex N(0,1), 2^26 samples (the page's
+# 40 ms at 6.5536 MHz is 2^18 samples; 256 times that fills the GPU).
+PFB_WORKLOADS = {
+    "pfb1024": dict(K=1024, D=512, Nh=8192, samples=1 << 26,
+                    description="K=1024 channels, D=512 (50% overlap), Nh=8192 Hamming "
+                                "windowed-sinc taps (cutoff 1/D of Nyquist), 2^26 samples"),
+    "pfb128": dict(K=128, D=64, Nh=1024, samples=1 << 26,
+                   description="K=128 channels, D=64 (50% overlap), Nh=1024 Hamming "
+                               "windowed-sinc taps (cutoff 1/D of Nyquist), 2^26 samples"),
+}
+
+
+def make_pfb_inputs(key: str, samples: Optional[int] = None):
+    """(taps float32 [Nh], x complex64 [samples]) of a channelizer workload."""
+    w = PFB_WORKLOADS[key]
+    h = hamming_sinc(w["Nh"], 1.0 / w["D"])
+    _, g_x, _ = rngs(BASE_SEED + 1000 + w["K"])
+    n = w["samples"] if samples is None else int(samples)
+    return h, complex_normal(g_x, n)
