@@ -127,18 +127,30 @@ __global__ __launch_bounds__(kThreads) void pfb_kernel(PfbArgs A) {
             // branch sums; the sample of tap n of branch k is at span index
             // j D + T K - 1 - n K - k
             const int base = j * A.D + T * K - 1 - tb;
+            // two registers' T samples are requested together before they
+            // are used, so 2 T reads are in flight instead of one
             float2 a[16];
-            static_for<0, 16>([&](auto Rr) {
-                constexpr int r = decltype(Rr)::value;
-                constexpr int kk = TB * firols::pass0_m<PG::gid>(r);
-                float2 s = make_float2(0.f, 0.f);
-                static_for<0, T>([&](auto Nn) {
-                    constexpr int n = decltype(Nn)::value;
-                    const float2 v = win[base - n * K - kk];
-                    s.x = fmaf(hr[n][r], v.x, s.x);
-                    s.y = fmaf(hr[n][r], v.y, s.y);
+            static_for<0, 8>([&](auto Qq) {
+                constexpr int r0 = 2 * decltype(Qq)::value;
+                float2 v[2][T];
+                static_for<0, 2>([&](auto Ii) {
+                    constexpr int i = decltype(Ii)::value;
+                    constexpr int kk = TB * firols::pass0_m<PG::gid>(r0 + i);
+                    static_for<0, T>([&](auto Nn) {
+                        constexpr int n = decltype(Nn)::value;
+                        v[i][n] = win[base - n * K - kk];
+                    });
                 });
-                a[r] = s;
+                static_for<0, 2>([&](auto Ii) {
+                    constexpr int i = decltype(Ii)::value;
+                    float2 s = make_float2(0.f, 0.f);
+                    static_for<0, T>([&](auto Nn) {
+                        constexpr int n = decltype(Nn)::value;
+                        s.x = fmaf(hr[n][r0 + i], v[i][n].x, s.x);
+                        s.y = fmaf(hr[n][r0 + i], v[i][n].y, s.y);
+                    });
+                    a[r0 + i] = s;
+                });
             });
             // the baseband phases W^{c t_m} of this thread's channels, requested
             // before the transform so their latency overlaps it
