@@ -18,6 +18,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -94,11 +95,18 @@ def _short(name: str) -> str:
     return name.split("(")[0].replace("void ", "")[:80]
 
 
+def _file_tag(kernel: str) -> str:
+    """A kernel name as a file-name part: ols_fused_kernel<12, false> ->
+    ols_fused_kernel_12_false."""
+    k = kernel.split("::")[-1]
+    return re.sub(r"[^A-Za-z0-9]+", "_", k).strip("_")
+
+
 def summarize_trace(args):
     """profiles/<kernel>_<workload>_kernel_trace.md from run_kernel_stats.csv."""
     rows = _csv_rows(args.summarize_trace, "kernel_stats.csv")
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    top = _short(rows[0]["Name"]).split("::")[-1].replace("<", "_").replace(">", "")
+    top = _file_tag(_short(rows[0]["Name"]))
     out = os.path.join(PROFILES_DIR, f"{top}_{args.workload}_kernel_trace.md")
     lines = [f"# Kernel trace: {args.workload} ({WORKLOAD_NOTE.get(args.workload, '')})", "",
              "Command (working directory /tmp):", "", "```", args.command, "```", "",
@@ -153,7 +161,7 @@ def summarize_pmc(args):
                          "fetch_scale": round(res["FETCH_SIZE"]["scale"], 4),
                          "write_scale": round(res["WRITE_SIZE"]["scale"], 4)}
     json.dump(db, open(path, "w"), indent=1, sort_keys=True)
-    top = sorted(kernels)[0].split("::")[-1].replace("<", "_").replace(">", "")
+    top = _file_tag(sorted(kernels)[0])
     out = os.path.join(PROFILES_DIR, f"{top}_{args.workload}_hbm_traffic.md")
     lines = [f"# HBM traffic: {args.workload} ({WORKLOAD_NOTE.get(args.workload, '')})", "",
              "Two counter runs of the same command, one per counter (working directory /tmp):",
@@ -191,13 +199,13 @@ def summarize_counters(args):
                        ("WRITE_SIZE", args.summarize_counters[1])):
         for r in _csv_rows(d, "counter_collection.csv"):
             k = r["Kernel_Name"]
-            if r["Counter_Name"] == counter and "ols_" in k and "plan_taps" not in k:
+            if (r["Counter_Name"] == counter and ("ols_" in k or "pfb_" in k)
+                    and "plan_taps" not in k):
                 per.setdefault(_short(k), {}).setdefault(counter, []).append(
                     float(r["Counter_Value"]))
     if not per:
         raise SystemExit("no filtering kernel in the counter runs")
-    top = max(per, key=lambda k: np.mean(per[k].get("FETCH_SIZE", [0.0])))
-    top = top.split("::")[-1].replace("<", "_").replace(">", "")
+    top = _file_tag(max(per, key=lambda k: np.mean(per[k].get("FETCH_SIZE", [0.0]))))
     out = os.path.join(PROFILES_DIR, f"{top}_{args.workload}_hbm_counters.md")
     lines = [f"# HBM counters: {args.workload} ({WORKLOAD_NOTE.get(args.workload, '')})", "",
              "Two counter runs of the same command, one per counter (working directory /tmp):",
@@ -253,7 +261,7 @@ def summarize_valu(args):
         db = {}
     db[args.workload] = rec
     json.dump(db, open(path, "w"), indent=1, sort_keys=True)
-    top = kern.split("::")[-1].replace("<", "_").replace(">", "")
+    top = _file_tag(kern)
     out = os.path.join(PROFILES_DIR, f"{top}_{args.workload}_valu.md")
     lines = [f"# VALU counters: {args.workload} ({WORKLOAD_NOTE.get(args.workload, '')})", "",
              "One counter run (working directory /tmp):", "", "```", args.command, "```", "",

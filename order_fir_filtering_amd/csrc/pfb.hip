@@ -30,11 +30,21 @@ using firols::static_for;
 namespace {
 
 constexpr int kThreads = 256;
-// LDS of one workgroup: the transforms' exchange areas, then the input span
-constexpr int kWinMax = 14336;
+// LDS of one workgroup: the transforms' exchange areas (4352 values for
+// every K), then the input span of at most win_cap(K, T) samples.  When a
+// tile of one output per transform group fits 5600 samples even at D = K,
+// the span is capped there so that two workgroups share a CU (80 KB of LDS
+// and 256 VGPRs each): one loads its next tile while the other computes.
+// Otherwise one workgroup takes the CU with a span of up to 14336.
+constexpr int kWinSmall = 5600;
+constexpr int kWinLarge = 14336;
+__host__ __device__ constexpr int win_cap(int K, int T) {
+    return T * K + (kThreads / (K / 16) - 1) * K <= kWinSmall ? kWinSmall : kWinLarge;
+}
 constexpr int kFill = 16;          // input loads in flight per thread while filling LDS
 // two floats as a clang vector, for the non-temporal store builtin
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int LOGK>
 struct PfbGeo {
@@ -55,11 +65,12 @@ __device__ __forceinline__ int bin_of_register(int tb, int r) {
 }
 
 template <int LOGK, int T>
-__global__ __launch_bounds__(kThreads) void pfb_kernel(PfbArgs A) {
+__global__ __launch_bounds__(kThreads, win_cap(1 << LOGK, T) == kWinSmall ? 2 : 1)
+void pfb_kernel(PfbArgs A) {
     using PG = PfbGeo<LOGK>;
     constexpr firols::Geo G = PG::G;
     constexpr int K = PG::K, TB = PG::TB;
-    __shared__ float2 smem[PG::FFT_LDS + kWinMax];
+    __shared__ float2 smem[PG::FFT_LDS + win_cap(K, T)];
     const int grp = threadIdx.x / TB;
     const int tb = threadIdx.x - grp * TB;
     float2 *fl = smem + grp * G.lds_stride;
@@ -155,10 +166,14 @@ __global__ __launch_bounds__(kThreads) void pfb_kernel(PfbArgs A) {
             // the baseband phases W^{c t_m} of this thread's channels, requested
             // before the transform so their latency overlaps it
             const int tm = (int)((A.t0 + (m % K) * A.D + A.D - 1) & (K - 1));
+            // slot jj of a thread is channel 2 (tb + TB (jj / 2)) + jj % 2: two
+            // neighbouring channels per lane, so a group's stores cover whole
+            // 128-byte lines even for small K
             float2 w[16];
             static_for<0, 16>([&](auto Jj) {
                 constexpr int jj = decltype(Jj)::value;
-                w[jj] = A.phase[((tb + TB * jj) * tm) & (K - 1)];
+                const int c = 2 * (tb + TB * (jj >> 1)) + (jj & 1);
+                w[jj] = A.phase[(c * tm) & (K - 1)];
             });
             firols::forward_all<PG::gid>(tb, a, fl, tw);
             // bins to channel order: bin b is channel (K - b) mod K
@@ -171,12 +186,21 @@ __global__ __launch_bounds__(kThreads) void pfb_kernel(PfbArgs A) {
             firols::wave_sync();
             if (m < A.nout) {
                 float2 *yr = A.y + m * K;
-                static_for<0, 16>([&](auto Jj) {
-                    constexpr int jj = decltype(Jj)::value;
-                    const int c = tb + TB * jj;
-                    const float2 v = fl[firols::lds_pad(G, c)];
-                    const f32x2 o = {v.x * w[jj].x - v.y * w[jj].y, v.x * w[jj].y + v.y * w[jj].x};
-                    __builtin_nontemporal_store(o, (f32x2 *)(yr + c));
+                static_for<0, 8>([&](auto Qq) {
+                    constexpr int q = decltype(Qq)::value;
+                    const int c = 2 * (tb + TB * q);
+                    const float2 v0 = fl[firols::lds_pad(G, c)];
+                    const float2 v1 = fl[firols::lds_pad(G, c + 1)];
+                    const float2 w0 = w[2 * q], w1 = w[2 * q + 1];
+                    const f32x2 o0 = {v0.x * w0.x - v0.y * w0.y, v0.x * w0.y + v0.y * w0.x};
+                    const f32x2 o1 = {v1.x * w1.x - v1.y * w1.y, v1.x * w1.y + v1.y * w1.x};
+                    if (A.y16) {
+                        const f32x4 o = {o0.x, o0.y, o1.x, o1.y};
+                        __builtin_nontemporal_store(o, (f32x4 *)(yr + c));
+                    } else {
+                        __builtin_nontemporal_store(o0, (f32x2 *)(yr + c));
+                        __builtin_nontemporal_store(o1, (f32x2 *)(yr + c + 1));
+                    }
                 });
             }
             firols::wave_sync();          // the exchange area is reused by the next output
@@ -227,8 +251,9 @@ int taps_per_branch(int K, int Nh) {
 
 int tile_outputs(int K, int D, int T) {
     const int fpw = kThreads / (K / 16);
-    if (T * K + (fpw - 1) * D > kWinMax) return 0;
-    int tm = (kWinMax - T * K) / D + 1;      // T K + (tm - 1) D <= kWinMax
+    const int cap = win_cap(K, T);
+    if (T * K + (fpw - 1) * D > cap) return 0;
+    int tm = (cap - T * K) / D + 1;          // T K + (tm - 1) D <= cap
     tm -= tm % fpw;
     return tm > 8 * fpw ? 8 * fpw : tm;
 }

@@ -22,6 +22,7 @@ struct PfbArgs {
     int K, D, Nh;
     int TM;                 // outputs per workgroup tile
     int t0;                 // stream time of x[0], mod K
+    int y16;                // y is 16-byte aligned: two channels per store
 };
 
 constexpr int kMinLogK = 6;

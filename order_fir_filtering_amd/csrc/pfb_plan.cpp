@@ -147,6 +147,7 @@ int fir_pfb_execute(fir_pfb_plan_t p, const void *x_dev, void *y_dev, int64_t ns
     a.Nh = p->Nh;
     a.TM = p->TM;
     a.t0 = (int)(p->pos % p->K);
+    a.y16 = ((uintptr_t)y_dev & 15) == 0;
     if (firpfb::launch(a, p->T, p->max_groups, (hipStream_t)stream) != hipSuccess)
         return FIR_OLS_ERR_HIP;
     if (p->Nh > 1) p->parity ^= 1;

@@ -165,3 +165,24 @@ def test_pfb_argument_checks():
         fo.fir_pfb_execute(c.handle, x, y, 0, None)        # no-op
         assert c.get_state()[1] == 0
     torch.cuda.synchronize()
+
+
+def test_pfb_output_only_8_byte_aligned():
+    """An output pointer that is 8- but not 16-byte aligned takes the
+    one-channel-per-store path; the results are the same."""
+    import torch
+    K, D, Nh = 64, 32, 300
+    rng = np.random.default_rng(8)
+    h = rng.standard_normal(Nh).astype(np.float32)
+    x = W.complex_normal(rng, 90 * D)
+    xd = to_dev(x)
+    buf = torch.zeros(x.size // D * K + 1, dtype=torch.complex64, device="cuda")
+    with fo.Channelizer(K, D, Nh) as c:
+        c.set_taps(h)
+        fo.fir_pfb_execute(c.handle, xd, buf.data_ptr() + 8, x.size, None)
+        torch.cuda.synchronize()
+    y = buf.cpu().numpy()[1:].reshape(x.size // D, K)
+    ref = oracle.pfb_channelize(h, x, K, D)
+    check(y, ref, h, x, None, "output at an odd element")
+    y16, _, _ = run(K, D, h, x, [x.size])
+    np.testing.assert_array_equal(y, y16)
