@@ -147,7 +147,7 @@ int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev,
  * and fir_ols_get_state hold the two rows' states packed the same way.
  * Stream-ordered and asynchronous like fir_ols_execute.
  * FIR_OLS_ERR_UNSUPPORTED unless the filter was set by fir_ols_set_taps
- * with real taps and N <= 16384; FIR_OLS_ERR_ALIGN for pointers not 4-byte
+ * with real taps (any N); FIR_OLS_ERR_ALIGN for pointers not 4-byte
  * aligned; other errors as fir_ols_execute.
  */
 int fir_ols_execute_real(fir_ols_plan_t p, const void *x_dev, void *y_dev,

@@ -1,0 +1,75 @@
+// Argument structures and size limits shared by the overlap-save kernels
+// and the host code that launches them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace firols {
+
+// Arguments of one overlap-save call over nchan channels.
+struct FusedArgs {
+    const float2 *x;        // [nchan][stride] input
+    float2 *y;              // [nchan][stride] output
+    const float2 *s0_old;   // [nchan][M-1] state read by this call (may be null if M == 1)
+    float2 *s0_new;         // [nchan][M-1] state written by this call
+    const float2 *H;        // N values, kernel order, scaled by 1/N
+    const float2 *tw;       // twiddle table of the transform
+    int64_t nsamples;       // samples per channel in this call (> 0)
+    int64_t stride;         // elements between channel starts
+    int64_t nblk;           // blocks per channel = ceil(nsamples / L)
+    int M;                  // taps
+    int L;                  // kept outputs per block
+    int nchan;
+};
+
+// Arguments of one call of the split (N = 65536) path.
+struct SplitArgs {
+    const float2 *x;        // [nchan][stride] input
+    float2 *y;              // [nchan][stride] output
+    const float2 *s0_old;   // [nchan][M-1] state read by this call
+    float2 *s0_new;         // [nchan][M-1] state written by this call
+    const float2 *H;        // RT * Ns values: bins k0 + RT k' in sub-kernel order, / N
+    const float2 *tw;       // twiddle table of the Ns-point sub-transform
+    const float2 *tw_top;   // RT * Ns values W_N^{q k0}, k0 = 0 .. RT-1 (row 0 all ones)
+    float2 *scratch;        // one slot of RT * Ns values per resident workgroup
+    int64_t nsamples;       // samples per channel in this call (> 0)
+    int64_t stride;         // elements between channel starts
+    int64_t nblk;           // blocks per channel
+    int M;
+    int L;
+    int nchan;
+};
+
+// Arguments of one batch of the multi-pass path (N = 2^17 .. 2^20): the
+// units (channel, block) u0 .. u0 + nu - 1 of a call, unit = c * nblk + i.
+struct MultiArgs {
+    const float2 *x;        // [nchan][stride] input
+    float2 *y;              // [nchan][stride] output
+    const float2 *s0_old;   // [nchan][M-1] state read by this call
+    float2 *s0_new;         // [nchan][M-1] state written by this call
+    const float2 *H;        // RT * Ns values: bins k0 + RT k' in sub-kernel order, / N
+    const float2 *tw;       // twiddle table of the Ns-point sub-transform
+    const float2 *tw_top;   // W_N^{q k0} factors: [RT][256] (q mod 256), then [RT][Ns/256]
+    float2 *scratch;        // [nu][RT][Ns]: the sub-sequences, then their convolutions
+    int64_t nsamples;       // samples per channel in this call (> 0)
+    int64_t stride;         // elements between channel starts
+    int64_t nblk;           // blocks per channel
+    int64_t u0;             // first unit of the batch
+    int nu;                 // units in the batch
+    int M;
+    int L;
+    int nchan;
+};
+
+// Largest log2(N) the LDS-resident kernel covers; N = 2^kBigLogN takes the
+// half-resident kernel, N = 2^kSplitLogN the split path, larger N (up to
+// kMaxLogN) the multi-pass path.
+constexpr int kFusedMaxLogN = 14;
+constexpr int kBigLogN = 15;
+constexpr int kSplitLogN = 16;
+constexpr int kMaxLogN = 20;
+constexpr int kMinLogN = 3;
+
+}  // namespace firols

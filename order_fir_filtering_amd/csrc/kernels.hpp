@@ -1,75 +1,16 @@
-// Internal interface between the C ABI (plan.cpp) and the HIP kernels.
+// Internal interface between the C ABI (plan.cpp) and the HIP kernels:
+// the launch and table-building functions (host side).  The argument
+// structures and size limits the kernels are compiled against are in
+// kernel_args.hpp.
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
+#include "kernel_args.hpp"
+
 namespace firols {
-
-// Arguments of one overlap-save call over nchan channels.
-struct FusedArgs {
-    const float2 *x;        // [nchan][stride] input
-    float2 *y;              // [nchan][stride] output
-    const float2 *s0_old;   // [nchan][M-1] state read by this call (may be null if M == 1)
-    float2 *s0_new;         // [nchan][M-1] state written by this call
-    const float2 *H;        // N values, kernel order, scaled by 1/N
-    const float2 *tw;       // twiddle table of the transform
-    int64_t nsamples;       // samples per channel in this call (> 0)
-    int64_t stride;         // elements between channel starts
-    int64_t nblk;           // blocks per channel = ceil(nsamples / L)
-    int M;                  // taps
-    int L;                  // kept outputs per block
-    int nchan;
-};
-
-// Arguments of one call of the split (N = 65536) path.
-struct SplitArgs {
-    const float2 *x;        // [nchan][stride] input
-    float2 *y;              // [nchan][stride] output
-    const float2 *s0_old;   // [nchan][M-1] state read by this call
-    float2 *s0_new;         // [nchan][M-1] state written by this call
-    const float2 *H;        // RT * Ns values: bins k0 + RT k' in sub-kernel order, / N
-    const float2 *tw;       // twiddle table of the Ns-point sub-transform
-    const float2 *tw_top;   // RT * Ns values W_N^{q k0}, k0 = 0 .. RT-1 (row 0 all ones)
-    float2 *scratch;        // one slot of RT * Ns values per resident workgroup
-    int64_t nsamples;       // samples per channel in this call (> 0)
-    int64_t stride;         // elements between channel starts
-    int64_t nblk;           // blocks per channel
-    int M;
-    int L;
-    int nchan;
-};
-
-// Arguments of one batch of the multi-pass path (N = 2^17 .. 2^20): the
-// units (channel, block) u0 .. u0 + nu - 1 of a call, unit = c * nblk + i.
-struct MultiArgs {
-    const float2 *x;        // [nchan][stride] input
-    float2 *y;              // [nchan][stride] output
-    const float2 *s0_old;   // [nchan][M-1] state read by this call
-    float2 *s0_new;         // [nchan][M-1] state written by this call
-    const float2 *H;        // RT * Ns values: bins k0 + RT k' in sub-kernel order, / N
-    const float2 *tw;       // twiddle table of the Ns-point sub-transform
-    const float2 *tw_top;   // W_N^{q k0} factors: [RT][256] (q mod 256), then [RT][Ns/256]
-    float2 *scratch;        // [nu][RT][Ns]: the sub-sequences, then their convolutions
-    int64_t nsamples;       // samples per channel in this call (> 0)
-    int64_t stride;         // elements between channel starts
-    int64_t nblk;           // blocks per channel
-    int64_t u0;             // first unit of the batch
-    int nu;                 // units in the batch
-    int M;
-    int L;
-    int nchan;
-};
-
-// Largest log2(N) the LDS-resident kernel covers; N = 2^kBigLogN takes the
-// half-resident kernel, N = 2^kSplitLogN the split path, larger N (up to
-// kMaxLogN) the multi-pass path.
-constexpr int kFusedMaxLogN = 14;
-constexpr int kBigLogN = 15;
-constexpr int kSplitLogN = 16;
-constexpr int kMaxLogN = 20;
-constexpr int kMinLogN = 3;
 
 // The table builders take a geometry id (geo_id(logn, logp)); a plain
 // log2(N) selects the default geometry of that size.
@@ -98,7 +39,7 @@ hipError_t launch_plan_taps(int logn, const float2 *taps_padded, float2 *H,
 // table builders), resident workgroups, launches.
 int big_geometry();
 int big_max_groups(int device);
-hipError_t launch_big(const FusedArgs &a, int max_groups, hipStream_t stream);
+hipError_t launch_big(const FusedArgs &a, int max_groups, hipStream_t stream, bool real = false);
 hipError_t launch_big_plan_taps(const float2 *taps_padded, float2 *H, const float2 *tw,
                                 hipStream_t stream);
 // Split path (N = 65536): radix of the split (N / 32768; 1 when
@@ -110,7 +51,8 @@ void build_split_twiddles(int logn, float2 *sub_tw, float2 *top_tw);
 void build_split_h_permutation(int logn, int64_t *perm);
 int64_t split_slot_elems(int logn);
 int split_max_groups(int device);
-hipError_t launch_split(int logn, const SplitArgs &a, int max_groups, hipStream_t stream);
+hipError_t launch_split(int logn, const SplitArgs &a, int max_groups, hipStream_t stream,
+                        bool real = false);
 
 // Multi-pass path (N = 2^17 .. 2^20): top-pass twiddle table size and
 // builder (the sub-transform shares the split path's tables and H order),
@@ -120,7 +62,8 @@ int64_t multi_top_twiddle_count(int logn);
 void build_multi_top_twiddles(int logn, float2 *top_tw);
 int multi_batch_units(int logn);
 int multi_max_groups(int device);
-hipError_t launch_multi(int logn, const MultiArgs &a, int max_groups, hipStream_t stream);
+hipError_t launch_multi(int logn, const MultiArgs &a, int max_groups, hipStream_t stream,
+                        bool real = false);
 
 // dst[i] = src ? src[i] : 0 for i < count.
 hipError_t launch_copy(float2 *dst, const float2 *src, int64_t count,

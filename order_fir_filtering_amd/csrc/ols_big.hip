@@ -27,6 +27,50 @@ constexpr int kStaggerGroups = 3;
 constexpr uint64_t kStaggerTicks = 1000;   // 10 us of the 100 MHz constant clock
 constexpr int kStaggerMinBlocks = 3;       // blocks per workgroup for the stagger to pay
 
+// Registers R0 .. R1-1 of block gb for real-pair channels (rows 2c and
+// 2c + 1 of a float32 [2 nchan][stride] array are the real and imaginary
+// parts of channel c): two range-checked 4-byte loads per point over the
+// block's valid input, plus, for the blocks that reach into the state, one
+// 8-byte load over the (complex) state; out-of-range loads read zero.
+template <int R0, int R1>
+__device__ __forceinline__ void gather_real_big(const FusedArgs &A, int64_t gb, int tb,
+                                                float2 (&v)[kBig.P]) {
+    const int64_t c = gb / A.nblk;
+    const int64_t i = gb - c * A.nblk;
+    const int Mm1 = A.M - 1;
+    const int64_t g0 = i * A.L - Mm1;
+    const int64_t xs = g0 > 0 ? g0 : 0;
+    int64_t xn = A.nsamples - xs;
+    xn = xn < 0 ? 0 : (xn > kBig.N ? kBig.N : xn);
+    const float *x1 = (const float *)A.x + 2 * c * A.stride + xs;
+    const __amdgpu_buffer_rsrc_t r1 = buf_rsrc(x1, (uint32_t)xn * 4u);
+    const __amdgpu_buffer_rsrc_t r2 = buf_rsrc(x1 + A.stride, (uint32_t)xn * 4u);
+    const int dx = (int)(g0 - xs) + tb;          // q + dx indexes the rows from xs
+    auto ld = [](__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    };
+    if (g0 >= 0) {
+        static_for<R0, R1>([&](auto Rr) {
+            constexpr int r = decltype(Rr)::value;
+            const uint32_t q = (uint32_t)(kBig.TB * pass0_m<kBigGid>(r) + dx);
+            v[r] = make_float2(ld(r1, q * 4u), ld(r2, q * 4u));
+        });
+    } else {
+        const __amdgpu_buffer_rsrc_t rs = buf_rsrc(A.s0_old + c * Mm1, (uint32_t)Mm1 * 8u);
+        const int ds = (int)(g0 + Mm1) + tb;     // q + ds indexes the state
+        static_for<R0, R1>([&](auto Rr) {
+            constexpr int r = decltype(Rr)::value;
+            constexpr int q = kBig.TB * pass0_m<kBigGid>(r);
+            const uint32_t qx = (uint32_t)(q + dx);
+            const float2 st = buf_load_cached(rs, (uint32_t)(q + ds) * 8u, 0);
+            v[r] = make_float2(ld(r1, qx * 4u) + st.x, ld(r2, qx * 4u) + st.y);
+        });
+    }
+}
+
+// REAL: the channels are pairs of real float32 rows, gathered by
+// gather_real_big and stored as two float rows.
+template <bool REAL>
 __global__ __launch_bounds__(kBig.TB) void ols_big_kernel(FusedArgs A) {
     __shared__ float2 lds[kHalfSlots + kTw1];
     float2 *lds_tw = lds + kHalfSlots;
@@ -45,7 +89,10 @@ __global__ __launch_bounds__(kBig.TB) void ols_big_kernel(FusedArgs A) {
     int64_t gb = unit_of(units, blockIdx.x, gridDim.x, 0);
     float2 a[kBig.P], r0[5], r1[5];
     if (gb >= 0) {
-        gather_block_wave<kBigGid, true, false>(A, gb, tb, a);
+        if constexpr (REAL)
+            gather_real_big<0, kBig.P>(A, gb, tb, a);
+        else
+            gather_block_wave<kBigGid, true, false>(A, gb, tb, a);
         const TwBig tw0{buf_rsrc(A.tw, (uint32_t)kBig.twoff[kBig.npass] * 8u), lds_tw, tb};
         load_pass0_rows<0>(r0, tw0);
         load_pass0_rows<1>(r1, tw0);
@@ -65,6 +112,9 @@ __global__ __launch_bounds__(kBig.TB) void ols_big_kernel(FusedArgs A) {
         if (yn > A.L) yn = A.L;
         const __amdgpu_buffer_rsrc_t ry =
             buf_rsrc(A.y + c * A.stride + i * A.L, (uint32_t)yn * 8u);
+        float *y1 = (float *)A.y + 2 * c * A.stride + i * A.L;
+        const __amdgpu_buffer_rsrc_t ry1 = buf_rsrc(y1, (uint32_t)yn * 4u);
+        const __amdgpu_buffer_rsrc_t ry2 = buf_rsrc(y1 + A.stride, (uint32_t)yn * 4u);
         const int qo = tb - Mm1;
         const __amdgpu_buffer_rsrc_t rtw = buf_rsrc(twp, (uint32_t)kBig.twoff[kBig.npass] * 8u);
         const __amdgpu_buffer_rsrc_t rh = buf_rsrc(hp, (uint32_t)kBig.N * 8u);
@@ -74,15 +124,26 @@ __global__ __launch_bounds__(kBig.TB) void ols_big_kernel(FusedArgs A) {
                 constexpr int u = decltype(Uu)::value;
                 static_for<0, 32>([&](auto J) {
                     constexpr int r = 32 * u + decltype(J)::value;
-                    buf_store(v[r], ry, (uint32_t)(qo + kBig.TB * pass0_m<kBigGid>(r)) * 8u);
+                    const uint32_t q = (uint32_t)(qo + kBig.TB * pass0_m<kBigGid>(r));
+                    if constexpr (REAL) {
+                        buf_store_f32(v[r].x, ry1, q * 4u);
+                        buf_store_f32(v[r].y, ry2, q * 4u);
+                    } else {
+                        buf_store(v[r], ry, q * 8u);
+                    }
                 });
             },
             [&](auto Uu, float2(&v)[64]) {
                 constexpr int u = decltype(Uu)::value;
-                if (gn >= 0) gather_block_wave<kBigGid, true, false, 32 * u, 32 * u + 32>(A, gn, tb, v);
+                if (gn >= 0) {
+                    if constexpr (REAL)
+                        gather_real_big<32 * u, 32 * u + 32>(A, gn, tb, v);
+                    else
+                        gather_block_wave<kBigGid, true, false, 32 * u, 32 * u + 32>(A, gn, tb, v);
+                }
             });
         if (i == A.nblk - 1)
-            carry_state<kBigGid>(A.nsamples, Mm1, tb, A.x + c * A.stride, A.s0_old + c * Mm1,
+            carry_state<kBigGid>(A.nsamples, Mm1, tb, ChanIn<REAL>(A, c), A.s0_old + c * Mm1,
                                  A.s0_new + c * Mm1);
         gb = gn;
     }
@@ -139,20 +200,29 @@ int big_max_groups(int device) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
         cus < 1)
         cus = 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ols_big_kernel, kBig.TB, 0) !=
-            hipSuccess ||
+    // the plan's workgroup count serves both variants: the smaller occupancy
+    int per_cu_real = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ols_big_kernel<false>, kBig.TB,
+                                                     0) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_real, ols_big_kernel<true>, kBig.TB,
+                                                     0) == hipSuccess &&
+        per_cu_real >= 1 && per_cu_real < per_cu)
+        per_cu = per_cu_real;
     return cus * per_cu;
 }
 
-hipError_t launch_big(const FusedArgs &a, int max_groups, hipStream_t stream) {
+hipError_t launch_big(const FusedArgs &a, int max_groups, hipStream_t stream, bool real) {
     const int64_t units = a.nblk * a.nchan;
     if (units <= 0) return hipErrorInvalidConfiguration;
     int64_t grid = units;
     if (grid > max_groups) grid = max_groups & ~7;    // persistent, multiple of 8
     if (grid <= 0) grid = units < max_groups ? units : max_groups;
-    hipLaunchKernelGGL(ols_big_kernel, dim3((unsigned)grid), dim3(kBig.TB), 0, stream, a);
+    if (real)
+        hipLaunchKernelGGL(ols_big_kernel<true>, dim3((unsigned)grid), dim3(kBig.TB), 0, stream, a);
+    else
+        hipLaunchKernelGGL(ols_big_kernel<false>, dim3((unsigned)grid), dim3(kBig.TB), 0, stream, a);
     return hipGetLastError();
 }
 

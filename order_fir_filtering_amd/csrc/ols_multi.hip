@@ -48,15 +48,44 @@ struct TopTw {
 
 // Sample n of block E (n in [0, N)) for a block that reaches past either
 // end of the input: the state in front, zeros past the end.
-__device__ __forceinline__ float2 edge_sample(const float2 *__restrict__ xc,
-                                              const float2 *__restrict__ sc, int64_t g,
-                                              int64_t nsamples, int Mm1) {
+template <class XC>
+__device__ __forceinline__ float2 edge_sample(const XC &xc, const float2 *__restrict__ sc,
+                                              int64_t g, int64_t nsamples, int Mm1) {
     if (g < 0) return sc[Mm1 + g];
     if (g < nsamples) return xc[g];
     return make_float2(0.f, 0.f);
 }
 
-template <int LRT>
+// Sample g of real-pair channel c (rows 2c and 2c + 1 of a float32
+// [2 nchan][stride] array are its real and imaginary parts).
+struct RealPair {
+    const float *__restrict__ x1;
+    const float *__restrict__ x2;
+    __device__ __forceinline__ float2 operator[](int64_t g) const {
+        return make_float2(x1[g], x2[g]);
+    }
+};
+
+template <bool REAL>
+struct MultiIn;
+template <>
+struct MultiIn<false> {
+    using T = const float2 *;
+    static __device__ __forceinline__ T chan(const MultiArgs &A, int64_t c) {
+        return A.x + c * A.stride;
+    }
+};
+template <>
+struct MultiIn<true> {
+    using T = RealPair;
+    static __device__ __forceinline__ T chan(const MultiArgs &A, int64_t c) {
+        const float *x1 = (const float *)A.x + 2 * c * A.stride;
+        return RealPair{x1, x1 + A.stride};
+    }
+};
+
+// REAL: real-pair channels, read as RealPair and written as two float rows.
+template <int LRT, bool REAL>
 __global__ __launch_bounds__(kQB) void ols_multi_top_kernel(MultiArgs A) {
     constexpr int RT = 1 << LRT;
     const int tid = threadIdx.x;
@@ -67,16 +96,15 @@ __global__ __launch_bounds__(kQB) void ols_multi_top_kernel(MultiArgs A) {
     const int64_t c = gb / A.nblk;
     const int64_t i = gb - c * A.nblk;
     const int Mm1 = A.M - 1;
-    const float2 *__restrict__ xc = A.x + c * A.stride;
+    const typename MultiIn<REAL>::T xc = MultiIn<REAL>::chan(A, c);
     const float2 *__restrict__ sc = A.s0_old + c * Mm1;
     const int64_t g0 = i * A.L - Mm1;
 
     float2 e[RT];
     if (g0 >= 0 && g0 + (int64_t)RT * kNs <= A.nsamples) {
-        const float2 *__restrict__ xb = xc + g0 + q;
         static_for<0, RT>([&](auto Jj) {
             constexpr int j = decltype(Jj)::value;
-            e[j] = xb[(int64_t)j * kNs];
+            e[j] = xc[g0 + q + (int64_t)j * kNs];
         });
     } else {
         static_for<0, RT>([&](auto Jj) {
@@ -104,7 +132,7 @@ __global__ __launch_bounds__(kQB) void ols_multi_top_kernel(MultiArgs A) {
     }
 }
 
-template <int LRT>
+template <int LRT, bool REAL>
 __global__ __launch_bounds__(kQB) void ols_multi_combine_kernel(MultiArgs A) {
     constexpr int RT = 1 << LRT;
     const int tid = threadIdx.x;
@@ -133,11 +161,18 @@ __global__ __launch_bounds__(kQB) void ols_multi_combine_kernel(MultiArgs A) {
     int64_t yn = A.nsamples - i * A.L;
     if (yn > A.L) yn = A.L;
     float2 *__restrict__ yb = A.y + c * A.stride + i * A.L;
+    float *__restrict__ y1 = (float *)A.y + 2 * c * A.stride + i * A.L;
     static_for<0, RT>([&](auto Jj) {
         constexpr int j = decltype(Jj)::value;
         const int64_t t = (int64_t)q + (int64_t)j * kNs - Mm1;
-        if (t >= 0 && t < yn)
-            __builtin_nontemporal_store(__builtin_bit_cast(f32x2, v[j]), (f32x2 *)(yb + t));
+        if (t >= 0 && t < yn) {
+            if constexpr (REAL) {
+                __builtin_nontemporal_store(v[j].x, y1 + t);
+                __builtin_nontemporal_store(v[j].y, y1 + A.stride + t);
+            } else {
+                __builtin_nontemporal_store(__builtin_bit_cast(f32x2, v[j]), (f32x2 *)(yb + t));
+            }
+        }
     });
 }
 
@@ -203,10 +238,10 @@ __global__ __launch_bounds__(kBig.TB) void ols_multi_sub_kernel(MultiArgs A, int
     }
 }
 
-template <int LRT>
+template <int LRT, bool REAL>
 hipError_t launch_batch(const MultiArgs &a, int max_groups, hipStream_t stream) {
     const dim3 gq((unsigned)a.nu * kQTiles);
-    hipLaunchKernelGGL(ols_multi_top_kernel<LRT>, gq, dim3(kQB), 0, stream, a);
+    hipLaunchKernelGGL((ols_multi_top_kernel<LRT, REAL>), gq, dim3(kQB), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t units = (int64_t)a.nu << LRT;
@@ -217,8 +252,16 @@ hipError_t launch_batch(const MultiArgs &a, int max_groups, hipStream_t stream) 
                        LRT);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(ols_multi_combine_kernel<LRT>, gq, dim3(kQB), 0, stream, a);
+    hipLaunchKernelGGL((ols_multi_combine_kernel<LRT, REAL>), gq, dim3(kQB), 0, stream, a);
     return hipGetLastError();
+}
+
+template <bool REAL>
+hipError_t launch_batch_r(int lrt, const MultiArgs &a, int max_groups, hipStream_t stream) {
+    return lrt == 2   ? launch_batch<2, REAL>(a, max_groups, stream)
+           : lrt == 3 ? launch_batch<3, REAL>(a, max_groups, stream)
+           : lrt == 4 ? launch_batch<4, REAL>(a, max_groups, stream)
+                      : launch_batch<5, REAL>(a, max_groups, stream);
 }
 
 }  // namespace
@@ -262,7 +305,8 @@ int multi_max_groups(int device) {
 
 // The call's units go through the scratch in batches of multi_batch_units;
 // each batch is its top, sub and combine launches, in stream order.
-hipError_t launch_multi(int logn, const MultiArgs &call, int max_groups, hipStream_t stream) {
+hipError_t launch_multi(int logn, const MultiArgs &call, int max_groups, hipStream_t stream,
+                        bool real) {
     const int lrt = logn - kBig.logn;
     const int64_t units = call.nblk * call.nchan;
     if (lrt < 2 || lrt > 5 || units <= 0) return hipErrorInvalidConfiguration;
@@ -271,10 +315,8 @@ hipError_t launch_multi(int logn, const MultiArgs &call, int max_groups, hipStre
         MultiArgs a = call;
         a.u0 = u0;
         a.nu = (int)(units - u0 < batch ? units - u0 : batch);
-        hipError_t e = lrt == 2   ? launch_batch<2>(a, max_groups, stream)
-                       : lrt == 3 ? launch_batch<3>(a, max_groups, stream)
-                       : lrt == 4 ? launch_batch<4>(a, max_groups, stream)
-                                  : launch_batch<5>(a, max_groups, stream);
+        hipError_t e = real ? launch_batch_r<true>(lrt, a, max_groups, stream)
+                            : launch_batch_r<false>(lrt, a, max_groups, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

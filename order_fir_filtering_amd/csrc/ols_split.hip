@@ -75,11 +75,13 @@ __device__ __forceinline__ void split_gather(float2 (&a)[64], int tb, const LOAD
 // c_0 read back from the slot; in groups of 8 points like the gather.  The
 // output descriptor covers the block's valid outputs only, so dropped and
 // past-the-end positions fall outside it.
-template <int U>
+template <int U, bool REAL>
 __device__ __forceinline__ void split_combine(const float2 (&v)[64], int tb, int qo,
                                               __amdgpu_buffer_rsrc_t rc0,
                                               __amdgpu_buffer_rsrc_t rtt1,
-                                              __amdgpu_buffer_rsrc_t ry) {
+                                              __amdgpu_buffer_rsrc_t ry,
+                                              __amdgpu_buffer_rsrc_t ry1,
+                                              __amdgpu_buffer_rsrc_t ry2) {
     constexpr int G = 8;
     float2 c0[2][G], w[2][G];
     auto issue = [&](auto Gx) {
@@ -102,15 +104,41 @@ __device__ __forceinline__ void split_combine(const float2 (&v)[64], int tb, int
             constexpr int r = 32 * U + g * G + i;
             constexpr int off = kBig.TB * pass0_m<kBigGid>(r);
             const float2 b1 = cmulc(v[r], w[g & 1][i]);
-            buf_store(cadd(c0[g & 1][i], b1), ry, (uint32_t)(qo + off) * 8u);
-            buf_store(csub(c0[g & 1][i], b1), ry, (uint32_t)(qo + off + kNs) * 8u);
+            const float2 y0 = cadd(c0[g & 1][i], b1), y1 = csub(c0[g & 1][i], b1);
+            if constexpr (REAL) {
+                buf_store_f32(y0.x, ry1, (uint32_t)(qo + off) * 4u);
+                buf_store_f32(y0.y, ry2, (uint32_t)(qo + off) * 4u);
+                buf_store_f32(y1.x, ry1, (uint32_t)(qo + off + kNs) * 4u);
+                buf_store_f32(y1.y, ry2, (uint32_t)(qo + off + kNs) * 4u);
+            } else {
+                buf_store(y0, ry, (uint32_t)(qo + off) * 8u);
+                buf_store(y1, ry, (uint32_t)(qo + off + kNs) * 8u);
+            }
         });
     });
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Channel c of real-pair input as complex samples: rows 2c and 2c + 1 of a
+// float32 [2 nchan][stride] array are its real and imaginary parts.
+struct RealRows {
+    const float *__restrict__ x1;
+    const float *__restrict__ x2;
+    __device__ __forceinline__ float2 operator[](int64_t g) const {
+        return make_float2(x1[g], x2[g]);
+    }
+};
+
+__device__ __forceinline__ float buf_load_f32_cached(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                     uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
 }  // namespace
 
+// REAL: the channels are pairs of real float32 rows (RealRows), read with
+// two 4-byte loads per point and stored as two float rows.
+template <bool REAL>
 __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
     __shared__ float2 lds[kHalfSlots + kTw1];
     float2 *lds_tw = lds + kHalfSlots;
@@ -148,11 +176,38 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
         const __amdgpu_buffer_rsrc_t rtt1 = buf_rsrc(ttp + kNs, (uint32_t)kNs * 8u);
         const TwBig tw{rtw, lds_tw, tb};
 
+        const float *x1 = (const float *)A.x + 2 * c * A.stride;
+        const float *x2 = x1 + A.stride;
         float2 a[64];
         if (g0 >= 0 && g0 + kRT * kNs <= A.nsamples) {
-            const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc + g0, (uint32_t)(kRT * kNs) * 8u);
+            if constexpr (REAL) {
+                const __amdgpu_buffer_rsrc_t rx1 = buf_rsrc(x1 + g0, (uint32_t)(kRT * kNs) * 4u);
+                const __amdgpu_buffer_rsrc_t rx2 = buf_rsrc(x2 + g0, (uint32_t)(kRT * kNs) * 4u);
+                split_gather(a, tb, [&](int j, int off) {
+                    const uint32_t o = (uint32_t)(off + j * kNs) * 4u;
+                    return make_float2(buf_load_f32_cached(rx1, (uint32_t)tb * 4u, o),
+                                       buf_load_f32_cached(rx2, (uint32_t)tb * 4u, o));
+                }, rtt1, ra1);
+            } else {
+                const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc + g0, (uint32_t)(kRT * kNs) * 8u);
+                split_gather(a, tb, [&](int j, int off) {
+                    return buf_load_cached(rx, (uint32_t)tb * 8u, (uint32_t)(off + j * kNs) * 8u);
+                }, rtt1, ra1);
+            }
+        } else if constexpr (REAL) {
+            const int64_t xs = g0 > 0 ? g0 : 0;
+            int64_t xn = A.nsamples - xs;
+            xn = xn < 0 ? 0 : (xn > kRT * kNs ? kRT * kNs : xn);
+            const __amdgpu_buffer_rsrc_t rx1 = buf_rsrc(x1 + xs, (uint32_t)xn * 4u);
+            const __amdgpu_buffer_rsrc_t rx2 = buf_rsrc(x2 + xs, (uint32_t)xn * 4u);
+            const __amdgpu_buffer_rsrc_t rs = buf_rsrc(sc, g0 < 0 ? (uint32_t)Mm1 * 8u : 0u);
+            const int dx = (int)(g0 - xs) + tb;
+            const int ds = (int)(g0 + Mm1) + tb;
             split_gather(a, tb, [&](int j, int off) {
-                return buf_load_cached(rx, (uint32_t)tb * 8u, (uint32_t)(off + j * kNs) * 8u);
+                const int q = off + j * kNs;
+                const float2 v = buf_load_cached(rs, (uint32_t)(q + ds) * 8u, 0);
+                return make_float2(buf_load_f32_cached(rx1, (uint32_t)(q + dx) * 4u, 0) + v.x,
+                                   buf_load_f32_cached(rx2, (uint32_t)(q + dx) * 4u, 0) + v.y);
             }, rtt1, ra1);
         } else {
             // first blocks (state in front) and the partial last block: two
@@ -198,16 +253,24 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
         if (yn > A.L) yn = A.L;
         const __amdgpu_buffer_rsrc_t ry =
             buf_rsrc(A.y + c * A.stride + i * A.L, (uint32_t)yn * 8u);
+        float *y1 = (float *)A.y + 2 * c * A.stride + i * A.L;
+        const __amdgpu_buffer_rsrc_t ry1 = buf_rsrc(y1, (uint32_t)yn * 4u);
+        const __amdgpu_buffer_rsrc_t ry2 = buf_rsrc(y1 + A.stride, (uint32_t)yn * 4u);
         const int qo = tb - Mm1;
         big_transform(
             tb, a, r0, r1, lds, tw, rh1,
             [&](auto Uu, const float2(&v)[64]) {
-                split_combine<decltype(Uu)::value>(v, tb, qo, rc0, rtt1, ry);
+                split_combine<decltype(Uu)::value, REAL>(v, tb, qo, rc0, rtt1, ry, ry1, ry2);
             },
             [&](auto, float2(&)[64]) {});
 
-        if (i == A.nblk - 1)
-            carry_state<kBigGid>(A.nsamples, Mm1, tb, xc, sc, A.s0_new + c * Mm1);
+        if (i == A.nblk - 1) {
+            if constexpr (REAL)
+                carry_state<kBigGid>(A.nsamples, Mm1, tb, RealRows{x1, x2}, sc,
+                                     A.s0_new + c * Mm1);
+            else
+                carry_state<kBigGid>(A.nsamples, Mm1, tb, xc, sc, A.s0_new + c * Mm1);
+        }
     }
 }
 
@@ -246,21 +309,32 @@ int split_max_groups(int device) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
         cus < 1)
         cus = 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ols_split_kernel, kBig.TB, 0) !=
-            hipSuccess ||
+    int per_cu_real = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ols_split_kernel<false>, kBig.TB,
+                                                     0) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_real, ols_split_kernel<true>,
+                                                     kBig.TB, 0) == hipSuccess &&
+        per_cu_real >= 1 && per_cu_real < per_cu)
+        per_cu = per_cu_real;
     return cus * per_cu;
 }
 
-hipError_t launch_split(int logn, const SplitArgs &a, int max_groups, hipStream_t stream) {
+hipError_t launch_split(int logn, const SplitArgs &a, int max_groups, hipStream_t stream,
+                        bool real) {
     const int64_t units = a.nblk * a.nchan;
     if (units <= 0 || split_radix(logn) != kRT) return hipErrorInvalidConfiguration;
     // one slot per workgroup: never more workgroups than the plan has slots
     int64_t grid = units;
     if (grid > max_groups) grid = max_groups & ~7;    // persistent, multiple of 8
     if (grid <= 0) grid = units < max_groups ? units : max_groups;
-    hipLaunchKernelGGL(ols_split_kernel, dim3((unsigned)grid), dim3(kBig.TB), 0, stream, a);
+    if (real)
+        hipLaunchKernelGGL(ols_split_kernel<true>, dim3((unsigned)grid), dim3(kBig.TB), 0, stream,
+                           a);
+    else
+        hipLaunchKernelGGL(ols_split_kernel<false>, dim3((unsigned)grid), dim3(kBig.TB), 0,
+                           stream, a);
     return hipGetLastError();
 }
 

@@ -317,7 +317,7 @@ int fir_ols_execute_real(fir_ols_plan_t p, const void *x_dev, void *y_dev, int64
                          int64_t row_stride, void *stream) {
     if (!p || nsamples < 0) return FIR_OLS_ERR_INVALID_ARG;
     if (!p->has_filter) return FIR_OLS_ERR_NO_FILTER;
-    if (!p->real_filter || p->logn > firols::kFusedMaxLogN) return FIR_OLS_ERR_UNSUPPORTED;
+    if (!p->real_filter) return FIR_OLS_ERR_UNSUPPORTED;
     if (nsamples == 0) return FIR_OLS_OK;
     if (!x_dev || !y_dev || row_stride < nsamples) return FIR_OLS_ERR_INVALID_ARG;
     if (((uintptr_t)x_dev | (uintptr_t)y_dev) & 3) return FIR_OLS_ERR_ALIGN;
@@ -327,21 +327,64 @@ int fir_ols_execute_real(fir_ols_plan_t p, const void *x_dev, void *y_dev, int64
     if (xa < ya + (uintptr_t)span && ya < xa + (uintptr_t)span) return FIR_OLS_ERR_ALIAS;
     if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
 
-    firols::FusedArgs a;
-    a.x = (const float2 *)x_dev;   // read as float32 rows by the real-pair kernels
-    a.y = (float2 *)y_dev;
-    a.s0_old = p->state[p->parity];
-    a.s0_new = p->state[p->parity ^ 1];
-    a.H = p->H;
-    a.tw = p->tw;
-    a.nsamples = nsamples;
-    a.stride = row_stride;
-    a.nblk = (nsamples + p->L - 1) / p->L;
-    a.M = (int)p->M;
-    a.L = (int)p->L;
-    a.nchan = (int)p->nchan;
-    const hipError_t e =
-        firols::launch_fused(p->logn, a, p->max_groups, (hipStream_t)stream, /*real=*/true);
+    // x and y are read and written as float32 rows by the real-pair kernels
+    const int64_t nblk = (nsamples + p->L - 1) / p->L;
+    hipError_t e = hipSuccess;
+    if (is_multi(p) || is_split(p)) {
+        firols::SplitArgs sa;
+        firols::MultiArgs ma;
+        if (is_multi(p)) {
+            ma.x = (const float2 *)x_dev;
+            ma.y = (float2 *)y_dev;
+            ma.s0_old = p->state[p->parity];
+            ma.s0_new = p->state[p->parity ^ 1];
+            ma.H = p->H;
+            ma.tw = p->tw;
+            ma.tw_top = p->tw_top;
+            ma.scratch = p->scratch;
+            ma.nsamples = nsamples;
+            ma.stride = row_stride;
+            ma.nblk = nblk;
+            ma.u0 = 0;
+            ma.nu = 0;
+            ma.M = (int)p->M;
+            ma.L = (int)p->L;
+            ma.nchan = (int)p->nchan;
+            e = firols::launch_multi(p->logn, ma, p->max_groups, (hipStream_t)stream, true);
+        } else {
+            sa.x = (const float2 *)x_dev;
+            sa.y = (float2 *)y_dev;
+            sa.s0_old = p->state[p->parity];
+            sa.s0_new = p->state[p->parity ^ 1];
+            sa.H = p->H;
+            sa.tw = p->tw;
+            sa.tw_top = p->tw_top;
+            sa.scratch = p->scratch;
+            sa.nsamples = nsamples;
+            sa.stride = row_stride;
+            sa.nblk = nblk;
+            sa.M = (int)p->M;
+            sa.L = (int)p->L;
+            sa.nchan = (int)p->nchan;
+            e = firols::launch_split(p->logn, sa, p->max_groups, (hipStream_t)stream, true);
+        }
+    } else {
+        firols::FusedArgs a;
+        a.x = (const float2 *)x_dev;
+        a.y = (float2 *)y_dev;
+        a.s0_old = p->state[p->parity];
+        a.s0_new = p->state[p->parity ^ 1];
+        a.H = p->H;
+        a.tw = p->tw;
+        a.nsamples = nsamples;
+        a.stride = row_stride;
+        a.nblk = nblk;
+        a.M = (int)p->M;
+        a.L = (int)p->L;
+        a.nchan = (int)p->nchan;
+        e = is_big(p) ? firols::launch_big(a, p->max_groups, (hipStream_t)stream, true)
+                      : firols::launch_fused(p->logn, a, p->max_groups, (hipStream_t)stream, true);
+    }
     if (e != hipSuccess) return FIR_OLS_ERR_HIP;
     if (p->M > 1) p->parity ^= 1;
     return FIR_OLS_OK;

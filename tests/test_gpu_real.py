@@ -5,8 +5,10 @@ Each real row is checked against the float64 oracle run on that row alone
 the row's filtered stream), so the packing of two rows into one complex
 channel is checked, not assumed.  Sizes cover every fused-kernel form
 (several blocks per wave, one wave per block, register-held and table-fed
-twiddles, pointer I/O at N = 16384), ragged lengths, padded row strides,
-calls carrying the state, and the argument checks.
+twiddles, pointer I/O at N = 16384), the half-resident (N = 32768), split
+(N = 65536) and multi-pass (N = 2^17, 2^18) kernels, ragged lengths,
+padded row strides, calls carrying the state, calls shorter than the
+state, and the argument checks.
 """
 import os
 
@@ -50,7 +52,11 @@ def _run_real(M, N, rows, calls, s0c=None, stride_pad=5):
 
 HREAL = {}
 CASES = [(65, 256, 2, [12288]), (257, 1024, 4, [30001, 7, 2000]), (1025, 4096, 2, [50000, 1, 9999]),
-         (2049, 8192, 2, [40000]), (4097, 16384, 2, [70000, 3]), (3, 8, 2, [100, 5])]
+         (2049, 8192, 2, [40000]), (4097, 16384, 2, [70000, 3]), (3, 8, 2, [100, 5]),
+         # the half-resident, split and multi-pass kernels
+         (8193, 32768, 2, [80000, 5, 30001]), (1, 32768, 2, [40000]),
+         (16385, 65536, 2, [150000, 7, 20000]), (30000, 65536, 4, [20000]),
+         (32769, 131072, 2, [250000, 3]), (100001, 262144, 2, [50000, 300000])]
 
 
 @pytest.mark.parametrize("M,N,nrow,calls", CASES)
@@ -123,9 +129,25 @@ def test_real_argument_checks():
         with pytest.raises(fo.FirOlsError) as e:
             fo.fir_ols_execute_real(p.handle, x, y, 100, 99)
         assert e.value.status == -1                       # stride below nsamples
-    with fo.Plan(8193, 32768, 1) as p:
-        p.set_taps(np.ones(8193, np.float32))
-        with pytest.raises(fo.FirOlsError) as e:
-            fo.fir_ols_execute_real(p.handle, x, y, 100, 100)
-        assert e.value.status == -2                       # N > 16384
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,N", [(8193, 32768), (16385, 65536), (32769, 131072)])
+def test_real_rows_equal_complex_channel_bitwise_large(M, N):
+    """As above for the large-N kernels: the real-pair forms compute what the
+    complex forms do on the packed channel, bit for bit."""
+    import torch
+    rng = np.random.default_rng(M)
+    h = (rng.standard_normal(M) / np.sqrt(M)).astype(np.float32)
+    HREAL[(M, N)] = h
+    n = 3 * (N - M + 1) + 777
+    rows = rng.standard_normal((2, n)).astype(np.float32)
+    y, _ = _run_real(M, N, rows, [n], stride_pad=0)
+    z = to_dev((rows[0] + 1j * rows[1]).astype(np.complex64)[None, :])
+    with fo.Plan(M, N, 1) as p:
+        p.set_taps(h)
+        yz = p.execute(z)
+        torch.cuda.synchronize()
+    yz = yz.cpu().numpy()[0]
+    np.testing.assert_array_equal(y[0], yz.real)
+    np.testing.assert_array_equal(y[1], yz.imag)
