@@ -50,7 +50,7 @@ def _device_chunked(N, M, h, x, s0, chunk, stride):
 
 
 CASES = [(1024, 257, 3, 20000), (4096, 1025, 1, 100000), (32768, 8193, 1, 120000),
-         (65536, 16385, 1, 150000)]
+         (65536, 16385, 1, 150000), (131072, 32769, 2, 300000)]
 
 
 @pytest.mark.parametrize("N,M,nchan,n", CASES)
@@ -139,7 +139,7 @@ def test_host_stream_argument_checks():
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("M", [1, 203, 1025, 5000])
+@pytest.mark.parametrize("M", [1, 203, 1025, 5000, 70000])
 def test_planner_choice_runs_and_matches_the_oracle(M):
     """A plan with the N that fir_ols_choose_n picks filters correctly."""
     N = fo.fir_ols_choose_n(M)
@@ -152,6 +152,8 @@ def test_planner_choice_runs_and_matches_the_oracle(M):
     with fo.Plan(M, N, 1) as p:
         p.set_taps(h)
         y = run_calls(p, x, [x.shape[1]], s0)
-    idx = np.arange(0, x.shape[1], 7)
+    n = x.shape[1]
+    idx = np.unique(np.concatenate([np.arange(min(n, 2000)), np.arange(0, n, max(7, n // 3000)),
+                                    [n - 1]]))
     ref = oracle.fir_direct_multi(h, x, s0, idx=idx, threads=THREADS)
     check(y[:, idx], ref, h, x, s0, f"planner M={M} N={N}")
