@@ -68,7 +68,11 @@ int fir_pfb_set_taps(fir_pfb_plan_t p, const float *h_host, int64_t Nh, void *st
  * The two ranges must not overlap.  Stream-ordered and asynchronous; the
  * state becomes the last Nh - 1 samples of {state, x} and the stream time
  * advances by nsamples, so consecutive calls equal one call over the
- * concatenated input.  Enqueues kernel launches only.
+ * concatenated input.  Enqueues kernel launches only, so a run of calls
+ * may be captured into a HIP graph; the stream time and the state buffer
+ * of each call are fixed at capture, so replays continue the stream when
+ * the captured run has an even number of calls (Nh > 1) and a multiple of
+ * K samples in all.
  */
 int fir_pfb_execute(fir_pfb_plan_t p, const void *x_dev, void *y_dev, int64_t nsamples,
                     void *stream);
