@@ -11,8 +11,10 @@
 //   v_k(m) = sum_n h(n K + k) xt(t_m - n K - k),
 // i.e. the branch filters of section 2.1, a K-point DFT across the
 // branches (its bin -c mod K for channel c), and the baseband phase
-// W^{c t_m}.  A workgroup takes a tile of TM consecutive outputs: it loads
-// the tile's input span (T K + (TM - 1) D samples) into LDS once, then each
+// W^{c t_m}.  A workgroup takes tiles of TM consecutive outputs in time
+// order: the tile's input span (T K + (TM - 1) D samples) sits in LDS, the
+// part it shares with the previous tile moved there from the previous span
+// and only the TM D new samples loaded from memory; then each
 // group of K / 16 threads (one K-point transform, 16 points per thread)
 // forms the K branch sums of one output from LDS with its taps held in
 // registers, transforms them, reorders the bins through LDS into channel
@@ -42,6 +44,7 @@ __host__ __device__ constexpr int win_cap(int K, int T) {
     return T * K + (kThreads / (K / 16) - 1) * K <= kWinSmall ? kWinSmall : kWinLarge;
 }
 constexpr int kFill = 16;          // input loads in flight per thread while filling LDS
+constexpr int kShift = 8;          // span values per thread per round of the LDS shift
 // two floats as a clang vector, for the non-temporal store builtin
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -93,17 +96,57 @@ void pfb_kernel(PfbArgs A) {
     const int span = T * K + (A.TM - 1) * A.D;
     const int64_t tiles = (A.nout + A.TM - 1) / A.TM;
 
-    for (int64_t it = 0;; ++it) {
-        const int64_t tile = firols::unit_of(tiles, blockIdx.x, gridDim.x, it);
-        if (tile < 0) break;
+    // this workgroup's tiles: one contiguous range (the XCD's eighth of the
+    // tiles split among its workgroups), taken in time order, so each tile
+    // after the first keeps the span it shares with the previous one in LDS
+    int64_t t_lo, t_hi;
+    {
+        const int G = gridDim.x, w = blockIdx.x;
+        if ((G & 7) == 0) {
+            const int per = G >> 3;
+            const int64_t chunk = (tiles + 7) >> 3;
+            const int64_t xlo = (int64_t)(w & 7) * chunk;
+            const int64_t xn = tiles - xlo < chunk ? (tiles - xlo > 0 ? tiles - xlo : 0) : chunk;
+            t_lo = xlo + xn * (w >> 3) / per;
+            t_hi = xlo + xn * ((w >> 3) + 1) / per;
+        } else {
+            t_lo = tiles * w / G;
+            t_hi = tiles * (w + 1) / G;
+        }
+    }
+    const int shift = A.TM * A.D;           // samples the span advances per tile
+    const int keep = span - shift;          // samples two neighbouring tiles share
+
+    for (int64_t tile = t_lo; tile < t_hi; ++tile) {
         const int64_t m0 = tile * A.TM;
         // input span of the tile: times (relative to x[0]) from w0 on
         const int64_t w0 = m0 * A.D + A.D - T * K;
         __syncthreads();                      // the previous tile's span is no longer read
+        int first = 0;                        // span entries still to load
+        if (tile > t_lo && keep > 0) {
+            // the shared part moves to the front: each round reads its
+            // values, waits for every thread, then writes them; a later
+            // round's sources lie past every earlier round's destinations
+            for (int e0 = 0; e0 < keep; e0 += kThreads * kShift) {
+                float2 v[kShift];
+                static_for<0, kShift>([&](auto Bb) {
+                    constexpr int b = decltype(Bb)::value;
+                    const int e = e0 + b * kThreads + (int)threadIdx.x;
+                    v[b] = e < keep ? win[shift + e] : make_float2(0.f, 0.f);
+                });
+                __syncthreads();
+                static_for<0, kShift>([&](auto Bb) {
+                    constexpr int b = decltype(Bb)::value;
+                    const int e = e0 + b * kThreads + (int)threadIdx.x;
+                    if (e < keep) win[e] = v[b];
+                });
+            }
+            first = keep;
+        }
         // kFill loads per thread are requested before the first is written
         // to LDS, so their latencies overlap
-        const bool inside = w0 >= 0 && w0 + span <= A.nsamples;
-        for (int e0 = threadIdx.x; e0 < span; e0 += kThreads * kFill) {
+        const bool inside = w0 + first >= 0 && w0 + span <= A.nsamples;
+        for (int e0 = first + (int)threadIdx.x; e0 < span; e0 += kThreads * kFill) {
             float2 v[kFill];
             if (inside) {
                 const float2 *__restrict__ xs = A.x + w0;
