@@ -799,8 +799,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": (f"ols_fused_kernel<{int(np.log2(w.N))}>" if w.N <= 16384 else
-                       "ols_big_kernel" if w.N == 32768 else "ols_split_kernel"),
+            "kernel": (f"ols_fused_kernel<{int(np.log2(w.N))}, false>" if w.N <= 16384 else
+                       "ols_big_kernel<false>" if w.N == 32768 else "ols_split_kernel<false>"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
