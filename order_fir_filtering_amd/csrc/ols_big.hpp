@@ -1,6 +1,7 @@
 // The 32768-point half-resident transform of one block (step 4 of the
 // method page's claim 1), shared by the N = 32768 kernel and the
-// sub-transforms of the N = 65536 split.
+// sub-transforms of the N = 65536 split and of the N = 2^17 .. 2^20
+// multi-pass path.
 //
 // The block (256 KB) does not fit the 160 KB LDS, so the transform is
 // ordered around that: pass 0 (stride 1024) runs on all 32768 points in
