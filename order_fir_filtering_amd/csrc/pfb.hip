@@ -96,9 +96,13 @@ void pfb_kernel(PfbArgs A) {
     const int span = T * K + (A.TM - 1) * A.D;
     const int64_t tiles = (A.nout + A.TM - 1) / A.TM;
 
-    // this workgroup's tiles: one contiguous range (the XCD's eighth of the
-    // tiles split among its workgroups), taken in time order, so each tile
-    // after the first keeps the span it shares with the previous one in LDS
+    // With one workgroup per CU (the large span), a workgroup takes one
+    // contiguous range of tiles (the XCD's eighth of the tiles split among
+    // its workgroups) in time order, so each tile after the first keeps the
+    // span it shares with the previous one in LDS.  With two workgroups per
+    // CU one loads while the other computes, and the tiles go round-robin
+    // over the workgroups of an XCD (no shift, whose registers would spill).
+    constexpr bool SLIDE = win_cap(K, T) == kWinLarge;
     int64_t t_lo, t_hi;
     {
         const int G = gridDim.x, w = blockIdx.x;
@@ -117,13 +121,21 @@ void pfb_kernel(PfbArgs A) {
     const int shift = A.TM * A.D;           // samples the span advances per tile
     const int keep = span - shift;          // samples two neighbouring tiles share
 
-    for (int64_t tile = t_lo; tile < t_hi; ++tile) {
+    for (int64_t it = 0;; ++it) {
+        int64_t tile;
+        if constexpr (SLIDE) {
+            tile = t_lo + it;
+            if (tile >= t_hi) break;
+        } else {
+            tile = firols::unit_of(tiles, blockIdx.x, gridDim.x, it);
+            if (tile < 0) break;
+        }
         const int64_t m0 = tile * A.TM;
         // input span of the tile: times (relative to x[0]) from w0 on
         const int64_t w0 = m0 * A.D + A.D - T * K;
         __syncthreads();                      // the previous tile's span is no longer read
         int first = 0;                        // span entries still to load
-        if (tile > t_lo && keep > 0) {
+        if (SLIDE && it > 0 && keep > 0) {
             // the shared part moves to the front: each round reads its
             // values, waits for every thread, then writes them; a later
             // round's sources lie past every earlier round's destinations
