@@ -446,6 +446,19 @@ def host_stream(args, inp, fo, torch, stream):
         e1.record(stream)
         torch.cuda.synchronize()
         rates[name] = 5 * xh.numel() * 8 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    # both directions at once (the streaming call's situation), on two
+    # default-priority streams
+    s_in, s_out = torch.cuda.Stream(), torch.cuda.Stream()
+    yd = torch.empty_like(xd)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        with torch.cuda.stream(s_in):
+            xd.copy_(xh, non_blocking=True)
+        with torch.cuda.stream(s_out):
+            yh.copy_(yd, non_blocking=True)
+    torch.cuda.synchronize()
+    duplex = 5 * xh.numel() * 8 / (time.perf_counter() - t0) / 1e9
     samples = w.nchan * w.samples
     link = min(rates["h2d"], rates["d2h"]) * 1e9 / 8 / 1e6
     return {"value": round(samples / (ms * 1e-3) / 1e6, 1), "unit": "Msamples/s",
@@ -453,6 +466,8 @@ def host_stream(args, inp, fo, torch, stream):
             "chunk": args.chunk or "default", "h2d_GBps": round(rates["h2d"], 1),
             "d2h_GBps": round(rates["d2h"], 1),
             "link_bound_Msamples": round(link, 1),
+            "duplex_GBps_each_way": round(duplex, 1),
+            "duplex_bound_Msamples": round(duplex * 1e9 / 8 / 1e6, 1),
             "note": "includes the host link; never the headline value"}
 
 
