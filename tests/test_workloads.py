@@ -62,3 +62,20 @@ def test_workload_shapes(key):
 def test_sample_indices():
     i = W.sample_indices(1, 1000, 50)
     assert i.size == 50 and np.all(np.diff(i) > 0) and i.min() >= 0 and i.max() < 1000
+
+
+@pytest.mark.parametrize("key", sorted(W.PFB_WORKLOADS))
+def test_channelizer_prototype_is_the_pages_design_call(key):
+    """The channelizer workloads' prototype is the window-method design the
+    channelizer page gives (section 2.2: a Hamming window, cutoff 1/D of
+    Nyquist), i.e. scipy's firwin(Nh, 1/D, window='hamming'); the input is
+    seeded and reproducible."""
+    w = W.PFB_WORKLOADS[key]
+    h, x = W.make_pfb_inputs(key, samples=4096)
+    ref = scipy.signal.firwin(w["Nh"], 1.0 / w["D"], window="hamming")
+    assert h.dtype == np.float32 and h.size == w["Nh"]
+    np.testing.assert_allclose(h, ref.astype(np.float32), rtol=0, atol=2e-9)
+    assert x.dtype == np.complex64 and x.shape == (4096,)
+    h2, x2 = W.make_pfb_inputs(key, samples=4096)
+    np.testing.assert_array_equal(x, x2)
+    assert w["K"] % w["D"] == 0 and w["samples"] % w["D"] == 0
