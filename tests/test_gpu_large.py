@@ -81,7 +81,8 @@ def _large_cases():
 
 @pytest.mark.parametrize("N,M,n,nchan,seed", _large_cases())
 def test_large_sizes(N, M, n, nchan, seed):
-    # N = 65536 takes its filter as H (set_taps is refused at that size)
+    # N = 65536 goes through the frequency-response entry here; its taps entry
+    # is covered by test_large_taps_and_freq_response_agree_and_stream
     say(f"large: N={N} M={M} n={n} nchan={nchan} seed={seed}")
     rng = np.random.default_rng(seed)
     h = (rng.standard_normal(M) + 1j * rng.standard_normal(M)).astype(np.complex64)

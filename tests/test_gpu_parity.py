@@ -58,7 +58,9 @@ def test_cfg2_four_calls_with_state_full():
     np.testing.assert_array_equal(st[0], oracle.state_next(inp.x[0], inp.s0[0], w.M))
 
 
-def test_cfg5_batched_channels_sampled():
+def test_cfg5_batched_channels_full():
+    """Every output of all 1024 channels and every channel's next state
+    (claim 1, step 3: each stream carries its own S0)."""
     inp = W.make_inputs("cfg5")
     w = inp.workload
     say(f"cfg5: M={w.M} N={w.N} nchan={w.nchan} n={w.samples}")
@@ -66,16 +68,9 @@ def test_cfg5_batched_channels_sampled():
         p.set_taps(inp.taps)
         y = run_calls(p, inp.x, w.calls, s0=inp.s0)
         st = p.get_state().cpu().numpy()
-    full = [0, 1, 511, w.nchan - 1]
-    ref = oracle_multi(inp.h_ref, inp.x[full], inp.s0[full])
-    check(y[full], ref, inp.h_ref, inp.x[full], inp.s0[full], "cfg5 full channels")
-    L = w.L
-    idx = np.unique(np.concatenate([
-        [0, 1, w.M - 2, w.M - 1, L - 1, L, 2 * L - 1, 85 * L - 1, 85 * L, w.samples - 1],
-        W.sample_indices(55, w.samples, 22)]))
-    ref_s = oracle_multi(inp.h_ref, inp.x, inp.s0, idx=idx)
-    check(y[:, idx], ref_s, inp.h_ref, inp.x, inp.s0, "cfg5 sampled, all channels")
-    for c in (0, 77, w.nchan - 1):
+    ref = oracle_multi(inp.h_ref, inp.x, inp.s0)
+    check(y, ref, inp.h_ref, inp.x, inp.s0, "cfg5 all channels, all outputs")
+    for c in range(w.nchan):
         np.testing.assert_array_equal(st[c], oracle.state_next(inp.x[c], inp.s0[c], w.M))
 
 
