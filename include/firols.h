@@ -154,6 +154,32 @@ int fir_ols_execute_real(fir_ols_plan_t p, const void *x_dev, void *y_dev,
                          int64_t nsamples, int64_t row_stride, void *stream);
 
 /*
+ * fir_ols_execute for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, layout, results, state carry and errors as
+ * fir_ols_execute (complex64 input), and the same kernels; the call
+ * allocates nothing.  The split (N = 65536) and multi-pass (N > 65536)
+ * kernels work in a fixed array of device memory inside the library,
+ * fir_ols_static_scratch_bytes() = 64 MiB, instead of the plan's own
+ * scratch area; each GPU the call runs on holds its own copy of that array
+ * until the process ends.  At N = 65536 at most 128 workgroups run (one per
+ * 512 KB slot of the array), so the call is slower than fir_ols_execute
+ * there; above 65536 the blocks go through the array in batches of as many
+ * as it holds.  Plans with N <= 32768 use no scratch.  A plan whose block
+ * would not fit the array gets FIR_OLS_ERR_UNSUPPORTED (no N the library
+ * accepts needs more than 8 MiB).  Every call on one GPU shares that GPU's
+ * array, whatever the plan: calls that may overlap in time on one GPU
+ * (different streams, different threads) race on it and give wrong
+ * results; order them on one stream.  The array's contents are whatever
+ * the last call left; the kernels write every value before they read it.
+ */
+int fir_ols_execute_static(fir_ols_plan_t p, const void *x_dev, void *y_dev,
+                           int64_t nsamples, int64_t chan_stride, void *stream);
+
+/* Size in bytes of the array fir_ols_execute_static works in. */
+int64_t fir_ols_static_scratch_bytes(void);
+
+/*
  * Host-resident streaming (claim 1, steps 2 and 6: the samples arrive from
  * host memory in chunks and the filtered chunks go back to it).  Filters
  * nsamples per channel exactly as fir_ols_execute would, carrying the

@@ -23,7 +23,8 @@ from .build import LIB as LIBRARY_PATH
 __all__ = [
     "FirOlsError", "Plan", "load_library", "LIBRARY_PATH", "EXPORTED",
     "fir_ols_plan", "fir_ols_set_taps", "fir_ols_set_freq_response",
-    "fir_ols_execute", "fir_ols_execute_host", "fir_ols_execute_real", "fir_ols_set_state",
+    "fir_ols_execute", "fir_ols_execute_host", "fir_ols_execute_real", "fir_ols_execute_static",
+    "fir_ols_static_scratch_bytes", "fir_ols_set_state",
     "fir_ols_get_state", "fir_ols_destroy", "fir_ols_block_length", "fir_ols_choose_n",
     "fir_ols_status_string", "Channelizer", "fir_pfb_plan", "fir_pfb_set_taps",
     "fir_pfb_execute", "fir_pfb_set_state", "fir_pfb_get_state", "fir_pfb_destroy",
@@ -32,7 +33,8 @@ __all__ = [
 # Every symbol include/firols.h and include/firpfb.h declare.
 EXPORTED = (
     "fir_ols_plan", "fir_ols_set_taps", "fir_ols_set_freq_response",
-    "fir_ols_execute", "fir_ols_execute_host", "fir_ols_execute_real", "fir_ols_set_state",
+    "fir_ols_execute", "fir_ols_execute_host", "fir_ols_execute_real", "fir_ols_execute_static",
+    "fir_ols_static_scratch_bytes", "fir_ols_set_state",
     "fir_ols_get_state", "fir_ols_destroy", "fir_ols_block_length", "fir_ols_choose_n",
     "fir_ols_status_string", "fir_pfb_plan", "fir_pfb_set_taps", "fir_pfb_execute",
     "fir_pfb_set_state", "fir_pfb_get_state", "fir_pfb_destroy",
@@ -75,6 +77,8 @@ def load_library(path: Optional[str] = None):
         "fir_ols_execute": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
         "fir_ols_execute_host": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
         "fir_ols_execute_real": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
+        "fir_ols_execute_static": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
+        "fir_ols_static_scratch_bytes": (_i64, []),
         "fir_ols_set_state": (_int, [_vp, _vp, _vp]),
         "fir_ols_get_state": (_int, [_vp, _vp, _vp]),
         "fir_ols_destroy": (_int, [_vp]),
@@ -161,6 +165,20 @@ def fir_ols_execute_real(plan: int, x, y, nsamples: int, row_stride: int, stream
     lib = load_library()
     _check(lib.fir_ols_execute_real(plan, _ptr(x), _ptr(y), nsamples, row_stride,
                                     _stream(stream)), "fir_ols_execute_real")
+
+
+def fir_ols_execute_static(plan: int, x, y, nsamples: int, chan_stride: int,
+                           stream=None) -> None:
+    """fir_ols_execute with the kernels' scratch in the library's fixed device
+    array (no allocation in the call)."""
+    lib = load_library()
+    _check(lib.fir_ols_execute_static(plan, _ptr(x), _ptr(y), nsamples, chan_stride,
+                                      _stream(stream)), "fir_ols_execute_static")
+
+
+def fir_ols_static_scratch_bytes() -> int:
+    """Size of the fixed device array fir_ols_execute_static works in."""
+    return int(load_library().fir_ols_static_scratch_bytes())
 
 
 def fir_ols_execute_host(plan: int, x, y, nsamples: int, chan_stride: int, chunk: int = 0,

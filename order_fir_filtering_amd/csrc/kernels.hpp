@@ -62,8 +62,9 @@ int64_t multi_top_twiddle_count(int logn);
 void build_multi_top_twiddles(int logn, float2 *top_tw);
 int multi_batch_units(int logn);
 int multi_max_groups(int device);
-hipError_t launch_multi(int logn, const MultiArgs &a, int max_groups, hipStream_t stream,
-                        bool real = false);
+// batch_units: blocks per batch, at most what the scratch holds.
+hipError_t launch_multi(int logn, const MultiArgs &a, int max_groups, int64_t batch_units,
+                        hipStream_t stream, bool real = false);
 
 // dst[i] = src ? src[i] : 0 for i < count.
 hipError_t launch_copy(float2 *dst, const float2 *src, int64_t count,

@@ -305,12 +305,12 @@ int multi_max_groups(int device) {
 
 // The call's units go through the scratch in batches of multi_batch_units;
 // each batch is its top, sub and combine launches, in stream order.
-hipError_t launch_multi(int logn, const MultiArgs &call, int max_groups, hipStream_t stream,
-                        bool real) {
+hipError_t launch_multi(int logn, const MultiArgs &call, int max_groups, int64_t batch_units,
+                        hipStream_t stream, bool real) {
     const int lrt = logn - kBig.logn;
     const int64_t units = call.nblk * call.nchan;
-    if (lrt < 2 || lrt > 5 || units <= 0) return hipErrorInvalidConfiguration;
-    const int64_t batch = multi_batch_units(logn);
+    if (lrt < 2 || lrt > 5 || units <= 0 || batch_units < 1) return hipErrorInvalidConfiguration;
+    const int64_t batch = batch_units;
     for (int64_t u0 = 0; u0 < units; u0 += batch) {
         MultiArgs a = call;
         a.u0 = u0;

@@ -133,6 +133,7 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
     if (ok && (split || multi)) {
         ok = hipMalloc(&p->tw_top, (size_t)ntop * sizeof(float2)) == hipSuccess &&
              hipMalloc(&p->scratch, (size_t)nscratch * sizeof(float2)) == hipSuccess;
+        p->scratch_elems = nscratch;
     }
     if (!ok) {
         (void)hipGetLastError();
@@ -238,25 +239,39 @@ int upload_freq_response(fir_ols_plan_t p, const float *H_host, hipStream_t s) {
 
 }  // namespace
 
-extern "C" {
+namespace firols {
 
-int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev, int64_t nsamples,
-                    int64_t chan_stride, void *stream) {
+// fir_ols_execute (real == false: complex64 [nchan][stride]) and
+// fir_ols_execute_real (real == true: float32 [2 nchan][stride]) on a
+// given scratch area of scratch_elems float2 values, which the split
+// (N = 65536) and multi-pass (N > 65536) kernels use: the split path runs at
+// most one workgroup per N-sample slot of it, the multi-pass path moves the
+// call's blocks through it in batches of as many blocks as it holds.
+int execute_with_scratch(fir_ols_plan_s *p, const void *x_dev, void *y_dev, int64_t nsamples,
+                         int64_t stride, void *stream, bool real, float2 *scratch,
+                         int64_t scratch_elems) {
     if (!p || nsamples < 0) return FIR_OLS_ERR_INVALID_ARG;
     if (!p->has_filter) return FIR_OLS_ERR_NO_FILTER;
+    if (real && !p->real_filter) return FIR_OLS_ERR_UNSUPPORTED;
     if (nsamples == 0) return FIR_OLS_OK;
-    if (!x_dev || !y_dev || chan_stride < nsamples) return FIR_OLS_ERR_INVALID_ARG;
-    if (((uintptr_t)x_dev | (uintptr_t)y_dev) & 7) return FIR_OLS_ERR_ALIGN;
-    if (chan_stride > ((int64_t)1 << 50) / p->nchan) return FIR_OLS_ERR_INVALID_ARG;
-    const int64_t span = ((p->nchan - 1) * chan_stride + nsamples) * (int64_t)sizeof(float2);
+    if (!x_dev || !y_dev || stride < nsamples) return FIR_OLS_ERR_INVALID_ARG;
+    const uintptr_t align = real ? 3 : 7;
+    if (((uintptr_t)x_dev | (uintptr_t)y_dev) & align) return FIR_OLS_ERR_ALIGN;
+    const int64_t rows = real ? 2 * p->nchan : p->nchan;
+    const int64_t item = real ? (int64_t)sizeof(float) : (int64_t)sizeof(float2);
+    if (stride > ((int64_t)1 << 50) / rows) return FIR_OLS_ERR_INVALID_ARG;
+    const int64_t span = ((rows - 1) * stride + nsamples) * item;
     const uintptr_t xa = (uintptr_t)x_dev, ya = (uintptr_t)y_dev;
     if (xa < ya + (uintptr_t)span && ya < xa + (uintptr_t)span) return FIR_OLS_ERR_ALIAS;
     if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
 
     const int64_t nblk = (nsamples + p->L - 1) / p->L;
+    const hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;
     if (is_multi(p)) {
-        firols::MultiArgs a;
+        const int64_t batch = scratch_elems / p->N;
+        if (!scratch || batch < 1) return FIR_OLS_ERR_UNSUPPORTED;
+        MultiArgs a;
         a.x = (const float2 *)x_dev;
         a.y = (float2 *)y_dev;
         a.s0_old = p->state[p->parity];
@@ -264,18 +279,22 @@ int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev, int64_t ns
         a.H = p->H;
         a.tw = p->tw;
         a.tw_top = p->tw_top;
-        a.scratch = p->scratch;
+        a.scratch = scratch;
         a.nsamples = nsamples;
-        a.stride = chan_stride;
+        a.stride = stride;
         a.nblk = nblk;
         a.u0 = 0;
         a.nu = 0;
         a.M = (int)p->M;
         a.L = (int)p->L;
         a.nchan = (int)p->nchan;
-        e = firols::launch_multi(p->logn, a, p->max_groups, (hipStream_t)stream);
+        e = launch_multi(p->logn, a, p->max_groups, batch, s, real);
     } else if (is_split(p)) {
-        firols::SplitArgs a;
+        // one slot per workgroup: never more workgroups than slots
+        const int64_t slots = scratch_elems / split_slot_elems(p->logn);
+        if (!scratch || slots < 1) return FIR_OLS_ERR_UNSUPPORTED;
+        const int groups = (int)(slots < p->max_groups ? slots : p->max_groups);
+        SplitArgs a;
         a.x = (const float2 *)x_dev;
         a.y = (float2 *)y_dev;
         a.s0_old = p->state[p->parity];
@@ -283,16 +302,16 @@ int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev, int64_t ns
         a.H = p->H;
         a.tw = p->tw;
         a.tw_top = p->tw_top;
-        a.scratch = p->scratch;
+        a.scratch = scratch;
         a.nsamples = nsamples;
-        a.stride = chan_stride;
+        a.stride = stride;
         a.nblk = nblk;
         a.M = (int)p->M;
         a.L = (int)p->L;
         a.nchan = (int)p->nchan;
-        e = firols::launch_split(p->logn, a, p->max_groups, (hipStream_t)stream);
+        e = launch_split(p->logn, a, groups, s, real);
     } else {
-        firols::FusedArgs a;
+        FusedArgs a;
         a.x = (const float2 *)x_dev;
         a.y = (float2 *)y_dev;
         a.s0_old = p->state[p->parity];
@@ -300,94 +319,33 @@ int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev, int64_t ns
         a.H = p->H;
         a.tw = p->tw;
         a.nsamples = nsamples;
-        a.stride = chan_stride;
+        a.stride = stride;
         a.nblk = nblk;
         a.M = (int)p->M;
         a.L = (int)p->L;
         a.nchan = (int)p->nchan;
-        e = is_big(p) ? firols::launch_big(a, p->max_groups, (hipStream_t)stream)
-                      : firols::launch_fused(p->logn, a, p->max_groups, (hipStream_t)stream);
+        e = is_big(p) ? launch_big(a, p->max_groups, s, real)
+                      : launch_fused(p->logn, a, p->max_groups, s, real);
     }
     if (e != hipSuccess) return FIR_OLS_ERR_HIP;
     if (p->M > 1) p->parity ^= 1;
     return FIR_OLS_OK;
 }
 
+}  // namespace firols
+
+extern "C" {
+
+int fir_ols_execute(fir_ols_plan_t p, const void *x_dev, void *y_dev, int64_t nsamples,
+                    int64_t chan_stride, void *stream) {
+    return firols::execute_with_scratch(p, x_dev, y_dev, nsamples, chan_stride, stream, false,
+                                        p ? p->scratch : nullptr, p ? p->scratch_elems : 0);
+}
+
 int fir_ols_execute_real(fir_ols_plan_t p, const void *x_dev, void *y_dev, int64_t nsamples,
                          int64_t row_stride, void *stream) {
-    if (!p || nsamples < 0) return FIR_OLS_ERR_INVALID_ARG;
-    if (!p->has_filter) return FIR_OLS_ERR_NO_FILTER;
-    if (!p->real_filter) return FIR_OLS_ERR_UNSUPPORTED;
-    if (nsamples == 0) return FIR_OLS_OK;
-    if (!x_dev || !y_dev || row_stride < nsamples) return FIR_OLS_ERR_INVALID_ARG;
-    if (((uintptr_t)x_dev | (uintptr_t)y_dev) & 3) return FIR_OLS_ERR_ALIGN;
-    if (row_stride > ((int64_t)1 << 50) / (2 * p->nchan)) return FIR_OLS_ERR_INVALID_ARG;
-    const int64_t span = ((2 * p->nchan - 1) * row_stride + nsamples) * (int64_t)sizeof(float);
-    const uintptr_t xa = (uintptr_t)x_dev, ya = (uintptr_t)y_dev;
-    if (xa < ya + (uintptr_t)span && ya < xa + (uintptr_t)span) return FIR_OLS_ERR_ALIAS;
-    if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
-
-    // x and y are read and written as float32 rows by the real-pair kernels
-    const int64_t nblk = (nsamples + p->L - 1) / p->L;
-    hipError_t e = hipSuccess;
-    if (is_multi(p) || is_split(p)) {
-        firols::SplitArgs sa;
-        firols::MultiArgs ma;
-        if (is_multi(p)) {
-            ma.x = (const float2 *)x_dev;
-            ma.y = (float2 *)y_dev;
-            ma.s0_old = p->state[p->parity];
-            ma.s0_new = p->state[p->parity ^ 1];
-            ma.H = p->H;
-            ma.tw = p->tw;
-            ma.tw_top = p->tw_top;
-            ma.scratch = p->scratch;
-            ma.nsamples = nsamples;
-            ma.stride = row_stride;
-            ma.nblk = nblk;
-            ma.u0 = 0;
-            ma.nu = 0;
-            ma.M = (int)p->M;
-            ma.L = (int)p->L;
-            ma.nchan = (int)p->nchan;
-            e = firols::launch_multi(p->logn, ma, p->max_groups, (hipStream_t)stream, true);
-        } else {
-            sa.x = (const float2 *)x_dev;
-            sa.y = (float2 *)y_dev;
-            sa.s0_old = p->state[p->parity];
-            sa.s0_new = p->state[p->parity ^ 1];
-            sa.H = p->H;
-            sa.tw = p->tw;
-            sa.tw_top = p->tw_top;
-            sa.scratch = p->scratch;
-            sa.nsamples = nsamples;
-            sa.stride = row_stride;
-            sa.nblk = nblk;
-            sa.M = (int)p->M;
-            sa.L = (int)p->L;
-            sa.nchan = (int)p->nchan;
-            e = firols::launch_split(p->logn, sa, p->max_groups, (hipStream_t)stream, true);
-        }
-    } else {
-        firols::FusedArgs a;
-        a.x = (const float2 *)x_dev;
-        a.y = (float2 *)y_dev;
-        a.s0_old = p->state[p->parity];
-        a.s0_new = p->state[p->parity ^ 1];
-        a.H = p->H;
-        a.tw = p->tw;
-        a.nsamples = nsamples;
-        a.stride = row_stride;
-        a.nblk = nblk;
-        a.M = (int)p->M;
-        a.L = (int)p->L;
-        a.nchan = (int)p->nchan;
-        e = is_big(p) ? firols::launch_big(a, p->max_groups, (hipStream_t)stream, true)
-                      : firols::launch_fused(p->logn, a, p->max_groups, (hipStream_t)stream, true);
-    }
-    if (e != hipSuccess) return FIR_OLS_ERR_HIP;
-    if (p->M > 1) p->parity ^= 1;
-    return FIR_OLS_OK;
+    return firols::execute_with_scratch(p, x_dev, y_dev, nsamples, row_stride, stream, true,
+                                        p ? p->scratch : nullptr, p ? p->scratch_elems : 0);
 }
 
 int fir_ols_set_state(fir_ols_plan_t p, const void *s0_dev, void *stream) {

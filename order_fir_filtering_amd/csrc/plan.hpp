@@ -21,6 +21,7 @@ struct fir_ols_plan_s {
     // split path (N = 65536) and multi-pass path (N = 2^17 .. 2^20)
     float2 *tw_top = nullptr;     // W_N^{q k0} (split: full rows; multi-pass: two factors)
     float2 *scratch = nullptr;    // split: max_groups slots of N values; multi-pass: a batch of blocks
+    int64_t scratch_elems = 0;    // float2 values at scratch
     // host-resident streaming (fir_ols_execute_host), created on first use
     int64_t hs_chunk = 0;                      // samples per channel of a staging slot
     float2 *hs_x[2] = {nullptr, nullptr};      // device input slots [nchan][hs_chunk]
@@ -31,3 +32,14 @@ struct fir_ols_plan_s {
 
 // Frees the host-streaming resources of a plan (no-op when never used).
 void release_host_stream(fir_ols_plan_s *p);
+
+namespace firols {
+// The filtering call behind fir_ols_execute (real == false) and
+// fir_ols_execute_real (real == true), with the kernels' scratch area given
+// explicitly (scratch_elems float2 values; only the N >= 65536 paths use
+// it).  Argument checks and status codes as fir_ols_execute;
+// FIR_OLS_ERR_UNSUPPORTED when the scratch cannot hold one N-sample slot.
+int execute_with_scratch(fir_ols_plan_s *p, const void *x_dev, void *y_dev, int64_t nsamples,
+                         int64_t stride, void *stream, bool real, float2 *scratch,
+                         int64_t scratch_elems);
+}  // namespace firols
