@@ -360,7 +360,7 @@ COMMON_DEVICE_SOURCES = ("kernel_args.hpp", "geometry.hpp", "dft.hpp", "ols_phas
 PATH_SOURCES = {
     "fused": ("ols_fused.hip",),
     "big": ("ols_big.hip", "ols_big.hpp"),
-    "split": ("ols_split.hip", "ols_big.hpp"),
+    "split": ("ols_split.hip", "ols_pair.hip", "ols_big.hpp"),
     "multi": ("ols_multi.hip", "ols_big.hpp"),
     "pfb": ("pfb.hip", "pfb.hpp"),
 }
@@ -642,7 +642,7 @@ def roofline_kernel(N: int) -> str:
     profiles print it."""
     return (f"ols_fused_kernel<{int(np.log2(N))}, false>" if N <= 16384 else
             "ols_big_kernel<false>" if N == 32768 else
-            "ols_split_kernel<false>" if N == 65536 else "ols_multi_sub_kernel<false>")
+            "ols_pair_kernel" if N == 65536 else "ols_multi_sub_kernel<false>")
 
 
 def measure(key, fo, torch, *, steps, warmup, timed_ms, warm_ms, cpu_budget, cpu_single_s,

@@ -67,10 +67,13 @@ enum {
  * Allocates the frequency response (aligned to 256 bytes, the page's
  * alignment rule in step 1), the twiddle tables and two state buffers of
  * nchan*(M-1) samples on the current device; for N = 65536 also a scratch
- * area of N samples (512 KB) per workgroup that fits on the device at once
- * (128 MiB on a 256-CU MI355X), and for N > 65536 a scratch area of
- * 128 MiB (blocks of N samples, at least one) through which the blocks of
- * a call pass in batches.  The state starts at zero.
+ * area of 512 KB for the synchronization flags of the two-workgroup kernel
+ * that filters the blocks whose L outputs are all valid, plus N samples
+ * (512 KB) per workgroup that fits on the device at once for the one-
+ * workgroup kernel that filters a call's partial last block (129 x 512 KB
+ * on a 256-CU MI355X); for N > 65536 a scratch area of 128 MiB (blocks of
+ * N samples, at least one) through which the blocks of a call pass in
+ * batches.  The state starts at zero.
  * No filter is set yet.  Synchronous.
  */
 int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan);
@@ -123,8 +126,10 @@ int fir_ols_set_freq_response(fir_ols_plan_t p, const float *H_host,
  * another block still reads).  The state of every channel becomes the last
  * M-1 samples of {S0, x} of that channel.
  * The call enqueues kernel launches only (no allocation, copy, fill or
- * synchronization): one for N <= 65536, three per batch of blocks for
- * N > 65536.  So a run of calls may be captured into a HIP graph;
+ * synchronization): one for N <= 32768; for N = 65536 a flag-clearing
+ * kernel and the two-workgroup kernel per batch of up to 65536 full
+ * blocks, and one launch for a partial last block; three per batch of
+ * blocks for N > 65536.  So a run of calls may be captured into a HIP graph;
  * replays then carry the state like the calls they were captured from,
  * provided the captured run has an even number of calls with M > 1 (the
  * two state buffers alternate, and the plan's record of which one is
@@ -162,9 +167,10 @@ int fir_ols_execute_real(fir_ols_plan_t p, const void *x_dev, void *y_dev,
  * kernels work in a fixed array of device memory inside the library,
  * fir_ols_static_scratch_bytes() = 64 MiB, instead of the plan's own
  * scratch area; each GPU the call runs on holds its own copy of that array
- * until the process ends.  At N = 65536 at most 128 workgroups run (one per
- * 512 KB slot of the array), so the call is slower than fir_ols_execute
- * there; above 65536 the blocks go through the array in batches of as many
+ * until the process ends.  At N = 65536 the first 512 KB hold the flags of
+ * the two-workgroup kernel and the rest 127 slots of 512 KB for the one-
+ * workgroup kernel of partial last blocks (at most 127 of its workgroups
+ * run); above 65536 the blocks go through the array in batches of as many
  * as it holds.  Plans with N <= 32768 use no scratch.  A plan whose block
  * would not fit the array gets FIR_OLS_ERR_UNSUPPORTED (no N the library
  * accepts needs more than 8 MiB).  Every call on one GPU shares that GPU's

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfirols.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["plan.cpp", "host_stream.cpp", "ols_fused.hip", "ols_big.hip", "ols_split.hip",
-           "ols_multi.hip", "pfb_plan.cpp", "pfb.hip", "static_scratch.hip"]
+           "ols_pair.hip", "ols_multi.hip", "pfb_plan.cpp", "pfb.hip", "static_scratch.hip"]
 ARCH = "gfx950"
 
 COMPILE_FLAGS = [

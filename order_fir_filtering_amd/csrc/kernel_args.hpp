@@ -37,10 +37,45 @@ struct SplitArgs {
     int64_t nsamples;       // samples per channel in this call (> 0)
     int64_t stride;         // elements between channel starts
     int64_t nblk;           // blocks per channel
+    int64_t blk0;           // first block of every channel this launch runs (blocks blk0 .. nblk-1)
     int M;
     int L;
     int nchan;
 };
+
+// Arguments of one launch of the paired N = 65536 kernel over the units
+// u0 .. u0 + nu - 1 (unit = c * nfull + i) of a call's full blocks.
+struct PairArgs {
+    const float2 *x;        // [nchan][stride] input
+    float2 *y;              // [nchan][stride] output
+    const float2 *s0_old;   // [nchan][M-1] state read by this call
+    float2 *s0_new;         // [nchan][M-1] state written by this call
+    const float2 *H;        // 2 * Ns values: bins k0 + 2 k' in sub-kernel order, / N
+    const float2 *tw;       // twiddle table of the Ns-point sub-transform
+    const float2 *tw_top;   // 2 * Ns values W_N^{q k0} (row 0 all ones)
+    unsigned *sync;         // kPairSyncHeader words (queue heads, exit count), then nu flags
+    int64_t nsamples;       // samples per channel in this call (> 0)
+    int64_t stride;         // elements between channel starts
+    int64_t nblk;           // blocks per channel
+    int64_t nfull;          // leading blocks per channel with L valid outputs
+    int64_t u0;             // first unit of the launch
+    int nu;                 // units in the launch
+    int nq;                 // work queues: one per XCD id 0 .. nq-1
+    int lead;               // blocks whose producers a queue hands out before their consumers
+    int M;
+    int L;
+    int nchan;
+};
+
+// Words of the paired kernel's synchronization area before the per-unit
+// flags: one queue head per XCD id (at most 16), the exit count, padding.
+constexpr int kPairSyncHeader = 32;
+constexpr int kPairMaxQueues = 16;
+constexpr int kPairExitWord = 16;
+// Units per launch of the paired kernel (its flags fill 256 KB, within
+// the 512 KB the split path's scratch reserves for them).
+constexpr int kPairMaxUnits = 65536;
+static_assert((kPairSyncHeader + kPairMaxUnits) * 4 <= 65536 * 8, "flags fit one slot");
 
 // Arguments of one batch of the multi-pass path (N = 2^17 .. 2^20): the
 // units (channel, block) u0 .. u0 + nu - 1 of a call, unit = c * nblk + i.

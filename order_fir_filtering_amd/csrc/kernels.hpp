@@ -53,6 +53,13 @@ int64_t split_slot_elems(int logn);
 int split_max_groups(int device);
 hipError_t launch_split(int logn, const SplitArgs &a, int max_groups, hipStream_t stream,
                         bool real = false);
+// Paired path (N = 65536, blocks with L valid outputs): work queues (one
+// per XCD id seen on the device), resident workgroups, and the launches of
+// one call (a counter reset and the kernel per batch of units).
+int pair_queue_count(int device);
+int pair_lead();
+int pair_max_groups(int device);
+hipError_t launch_pair(const PairArgs &a, int max_groups, hipStream_t stream);
 
 // Multi-pass path (N = 2^17 .. 2^20): top-pass twiddle table size and
 // builder (the sub-transform shares the split path's tables and H order),

@@ -28,28 +28,28 @@ constexpr int kNs = kBig.N;        // points of a sub-transform
 constexpr int kRT = 2;             // sub-transforms per block
 
 // a_0 of one block into the pass-0 layout (register r <-> q = tb + TB m)
-// and a_1 into the slot, reading E[q] and E[q + Ns] through load(j, TB m)
-// and W_N^q from the second row of the top twiddles.  E[q] of all points
-// is requested first; E[q + Ns] and the twiddle go in groups of 8 points,
-// the next group requested before the current one is used, so the
+// and a_1 into the slot, reading E[q] and E[q + Ns] through load(j, TB m);
+// W_N^q = W_N^tb W_N^{TB m}, the second factor from the LDS table wm (the
+// paired kernel forms it the same way, so both compute identical values).
+// E[q] of all points is requested first; E[q + Ns] goes in groups of 8
+// points, the next group requested before the current one is used, so the
 // registers in flight stay bounded.
 template <class LOAD>
 __device__ __forceinline__ void split_gather(float2 (&a)[64], int tb, const LOAD &load,
-                                             __amdgpu_buffer_rsrc_t rtt1,
+                                             float2 wt, const float2 *wm,
                                              __amdgpu_buffer_rsrc_t rslot) {
     static_for<0, 64>([&](auto Rr) {
         constexpr int r = decltype(Rr)::value;
         a[r] = load(0, kBig.TB * pass0_m<kBigGid>(r));
     });
     constexpr int G = 8;
-    float2 e[2][G], w[2][G];
+    float2 e[2][G];
     auto issue = [&](auto Gx) {
         constexpr int g = decltype(Gx)::value;
         static_for<0, G>([&](auto Ii) {
             constexpr int i = decltype(Ii)::value;
             constexpr int off = kBig.TB * pass0_m<kBigGid>(g * G + i);
             e[g & 1][i] = load(1, off);
-            w[g & 1][i] = buf_load_cached(rtt1, (uint32_t)tb * 8u, (uint32_t)off * 8u);
         });
     };
     issue(ic<0>{});
@@ -63,8 +63,8 @@ __device__ __forceinline__ void split_gather(float2 (&a)[64], int tb, const LOAD
             constexpr int r = g * G + i;
             const float2 d = csub(a[r], e[g & 1][i]);
             a[r] = cadd(a[r], e[g & 1][i]);
-            buf_store_cached(cmul(d, w[g & 1][i]), rslot, (uint32_t)tb * 8u,
-                             (uint32_t)(kBig.TB * pass0_m<kBigGid>(r)) * 8u);
+            buf_store_cached(cmul(d, cmul(wt, wm[pass0_m<kBigGid>(r)])), rslot,
+                             (uint32_t)tb * 8u, (uint32_t)(kBig.TB * pass0_m<kBigGid>(r)) * 8u);
         });
     });
     __builtin_amdgcn_sched_barrier(0);
@@ -77,20 +77,18 @@ __device__ __forceinline__ void split_gather(float2 (&a)[64], int tb, const LOAD
 // past-the-end positions fall outside it.
 template <int U, bool REAL>
 __device__ __forceinline__ void split_combine(const float2 (&v)[64], int tb, int qo,
-                                              __amdgpu_buffer_rsrc_t rc0,
-                                              __amdgpu_buffer_rsrc_t rtt1,
-                                              __amdgpu_buffer_rsrc_t ry,
+                                              __amdgpu_buffer_rsrc_t rc0, float2 wt,
+                                              const float2 *wm, __amdgpu_buffer_rsrc_t ry,
                                               __amdgpu_buffer_rsrc_t ry1,
                                               __amdgpu_buffer_rsrc_t ry2) {
     constexpr int G = 8;
-    float2 c0[2][G], w[2][G];
+    float2 c0[2][G];
     auto issue = [&](auto Gx) {
         constexpr int g = decltype(Gx)::value;
         static_for<0, G>([&](auto Ii) {
             constexpr int i = decltype(Ii)::value;
             constexpr int off = kBig.TB * pass0_m<kBigGid>(32 * U + g * G + i);
             c0[g & 1][i] = buf_load_cached(rc0, (uint32_t)tb * 8u, (uint32_t)off * 8u);
-            w[g & 1][i] = buf_load_cached(rtt1, (uint32_t)tb * 8u, (uint32_t)off * 8u);
         });
     };
     issue(ic<0>{});
@@ -103,7 +101,7 @@ __device__ __forceinline__ void split_combine(const float2 (&v)[64], int tb, int
             constexpr int i = decltype(Ii)::value;
             constexpr int r = 32 * U + g * G + i;
             constexpr int off = kBig.TB * pass0_m<kBigGid>(r);
-            const float2 b1 = cmulc(v[r], w[g & 1][i]);
+            const float2 b1 = cmulc(v[r], cmul(wt, wm[pass0_m<kBigGid>(r)]));
             const float2 y0 = cadd(c0[g & 1][i], b1), y1 = csub(c0[g & 1][i], b1);
             if constexpr (REAL) {
                 buf_store_f32(y0.x, ry1, (uint32_t)(qo + off) * 4u);
@@ -141,9 +139,13 @@ __device__ __forceinline__ float buf_load_f32_cached(__amdgpu_buffer_rsrc_t r, u
 template <bool REAL>
 __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
     __shared__ float2 lds[kHalfSlots + kTw1];
+    __shared__ float2 wm[64];
     float2 *lds_tw = lds + kHalfSlots;
     const int tb = threadIdx.x;
     for (int e = tb; e < kTw1; e += kBig.TB) lds_tw[e] = A.tw[kBig.twoff[1] + e];
+    // W_N^q = W_N^tb W_N^{TB m} for the points q = tb + TB m of a thread
+    if (tb < 64) wm[tb] = A.tw_top[kNs + kBig.TB * tb];
+    const float2 wt0 = A.tw_top[kNs + tb];
     // (the first barrier of the transform orders these writes before use)
     // this workgroup's slot: a_1, then c_0 (a thread reads back only the
     // positions it wrote)
@@ -151,7 +153,8 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
     const __amdgpu_buffer_rsrc_t ra1 = buf_rsrc(slot, (uint32_t)kNs * 8u);
     const __amdgpu_buffer_rsrc_t rc0 = buf_rsrc(slot + kNs, (uint32_t)kNs * 8u);
     const int Mm1 = A.M - 1;
-    const int64_t units = A.nblk * A.nchan;
+    const int64_t per_chan = A.nblk - A.blk0;    // blocks of each channel this launch runs
+    const int64_t units = per_chan * A.nchan;
     // pass-0 twiddle rows of both virtual threads, the same for every block
     float2 r0[5], r1[5];
     {
@@ -162,19 +165,22 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
     for (int64_t it = 0;; ++it) {
         const int64_t gb = unit_of(units, blockIdx.x, gridDim.x, it);
         if (gb < 0) break;
-        const int64_t c = gb / A.nblk;
-        const int64_t i = gb - c * A.nblk;
+        const int64_t c = gb / per_chan;
+        const int64_t i = A.blk0 + (gb - c * per_chan);
         const float2 *__restrict__ xc = A.x + c * A.stride;
         const float2 *__restrict__ sc = A.s0_old + c * Mm1;
         const int64_t g0 = i * A.L - Mm1;
         // table pointers re-derived per block so their loads stay in the loop
-        const float2 *twp = A.tw, *hp = A.H, *ttp = A.tw_top;
-        asm volatile("" : "+s"(twp), "+s"(hp), "+s"(ttp));
+        const float2 *twp = A.tw, *hp = A.H;
+        asm volatile("" : "+s"(twp), "+s"(hp));
         const __amdgpu_buffer_rsrc_t rtw = buf_rsrc(twp, (uint32_t)kBig.twoff[kBig.npass] * 8u);
         const __amdgpu_buffer_rsrc_t rh0 = buf_rsrc(hp, (uint32_t)kNs * 8u);
         const __amdgpu_buffer_rsrc_t rh1 = buf_rsrc(hp + kNs, (uint32_t)kNs * 8u);
-        const __amdgpu_buffer_rsrc_t rtt1 = buf_rsrc(ttp + kNs, (uint32_t)kNs * 8u);
         const TwBig tw{rtw, lds_tw, tb};
+        // (the empty asm keeps the 64 twiddle products, which do not depend
+        // on the block, from being hoisted out of the loop)
+        float2 wt = wt0;
+        asm volatile("" : "+v"(wt.x), "+v"(wt.y));
 
         const float *x1 = (const float *)A.x + 2 * c * A.stride;
         const float *x2 = x1 + A.stride;
@@ -187,12 +193,12 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
                     const uint32_t o = (uint32_t)(off + j * kNs) * 4u;
                     return make_float2(buf_load_f32_cached(rx1, (uint32_t)tb * 4u, o),
                                        buf_load_f32_cached(rx2, (uint32_t)tb * 4u, o));
-                }, rtt1, ra1);
+                }, wt, wm, ra1);
             } else {
                 const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc + g0, (uint32_t)(kRT * kNs) * 8u);
                 split_gather(a, tb, [&](int j, int off) {
                     return buf_load_cached(rx, (uint32_t)tb * 8u, (uint32_t)(off + j * kNs) * 8u);
-                }, rtt1, ra1);
+                }, wt, wm, ra1);
             }
         } else if constexpr (REAL) {
             const int64_t xs = g0 > 0 ? g0 : 0;
@@ -208,7 +214,7 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
                 const float2 v = buf_load_cached(rs, (uint32_t)(q + ds) * 8u, 0);
                 return make_float2(buf_load_f32_cached(rx1, (uint32_t)(q + dx) * 4u, 0) + v.x,
                                    buf_load_f32_cached(rx2, (uint32_t)(q + dx) * 4u, 0) + v.y);
-            }, rtt1, ra1);
+            }, wt, wm, ra1);
         } else {
             // first blocks (state in front) and the partial last block: two
             // range-checked loads per point, one over the valid input and one
@@ -225,7 +231,7 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
                 const float2 u = buf_load_cached(rx, (uint32_t)(q + dx) * 8u, 0);
                 const float2 v = buf_load_cached(rs, (uint32_t)(q + ds) * 8u, 0);
                 return make_float2(u.x + v.x, u.y + v.y);
-            }, rtt1, ra1);
+            }, wt, wm, ra1);
         }
 
         // first half-spectrum: c_0 to the slot, a_1 back from it
@@ -260,7 +266,7 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
         big_transform(
             tb, a, r0, r1, lds, tw, rh1,
             [&](auto Uu, const float2(&v)[64]) {
-                split_combine<decltype(Uu)::value, REAL>(v, tb, qo, rc0, rtt1, ry, ry1, ry2);
+                split_combine<decltype(Uu)::value, REAL>(v, tb, qo, rc0, wt, wm, ry, ry1, ry2);
             },
             [&](auto, float2(&)[64]) {});
 
@@ -323,8 +329,8 @@ int split_max_groups(int device) {
 
 hipError_t launch_split(int logn, const SplitArgs &a, int max_groups, hipStream_t stream,
                         bool real) {
-    const int64_t units = a.nblk * a.nchan;
-    if (units <= 0 || split_radix(logn) != kRT) return hipErrorInvalidConfiguration;
+    const int64_t units = (a.nblk - a.blk0) * a.nchan;
+    if (units <= 0 || a.blk0 < 0 || split_radix(logn) != kRT) return hipErrorInvalidConfiguration;
     // one slot per workgroup: never more workgroups than the plan has slots
     int64_t grid = units;
     if (grid > max_groups) grid = max_groups & ~7;    // persistent, multiple of 8

@@ -118,10 +118,18 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
     const int64_t ntop = multi   ? firols::multi_top_twiddle_count(logn)
                          : split ? firols::split_top_twiddle_count(logn)
                                  : 0;
+    // split: the paired kernel's flags (one slot's worth), then one slot per
+    // workgroup of the one-workgroup kernel
     const int64_t nscratch =
         multi   ? (int64_t)firols::multi_batch_units(logn) * N
-        : split ? (int64_t)p->max_groups * firols::split_slot_elems(logn)
+        : split ? (int64_t)(p->max_groups + 1) * firols::split_slot_elems(logn)
                 : 0;
+    if (split) {
+        p->pair_nq = firols::pair_queue_count(p->device);
+        p->pair_lead = firols::pair_lead();
+        p->pair_groups = firols::pair_max_groups(p->device);
+        (void)hipGetLastError();
+    }
     const size_t sbytes = (size_t)state_len(p) * sizeof(float2);
     bool ok = hipMalloc(&p->H, N * sizeof(float2)) == hipSuccess &&
               hipMalloc(&p->tw, (size_t)(ntw > 0 ? ntw : 1) * sizeof(float2)) == hipSuccess &&
@@ -290,26 +298,58 @@ int execute_with_scratch(fir_ols_plan_s *p, const void *x_dev, void *y_dev, int6
         a.nchan = (int)p->nchan;
         e = launch_multi(p->logn, a, p->max_groups, batch, s, real);
     } else if (is_split(p)) {
-        // one slot per workgroup: never more workgroups than slots
-        const int64_t slots = scratch_elems / split_slot_elems(p->logn);
+        // the scratch starts with the paired kernel's flags (one slot's
+        // worth), then one slot per workgroup of the one-workgroup kernel
+        const int64_t slot = split_slot_elems(p->logn);
+        const int64_t slots = scratch_elems / slot - 1;
         if (!scratch || slots < 1) return FIR_OLS_ERR_UNSUPPORTED;
-        const int groups = (int)(slots < p->max_groups ? slots : p->max_groups);
-        SplitArgs a;
-        a.x = (const float2 *)x_dev;
-        a.y = (float2 *)y_dev;
-        a.s0_old = p->state[p->parity];
-        a.s0_new = p->state[p->parity ^ 1];
-        a.H = p->H;
-        a.tw = p->tw;
-        a.tw_top = p->tw_top;
-        a.scratch = scratch;
-        a.nsamples = nsamples;
-        a.stride = stride;
-        a.nblk = nblk;
-        a.M = (int)p->M;
-        a.L = (int)p->L;
-        a.nchan = (int)p->nchan;
-        e = launch_split(p->logn, a, groups, s, real);
+        // blocks whose L outputs are all valid go to the paired kernel
+        // (complex input); a partial last block, and real-pair input, to the
+        // one-workgroup kernel
+        const int64_t nfull = real ? 0 : nsamples / p->L;
+        if (nfull > 0) {
+            PairArgs a;
+            a.x = (const float2 *)x_dev;
+            a.y = (float2 *)y_dev;
+            a.s0_old = p->state[p->parity];
+            a.s0_new = p->state[p->parity ^ 1];
+            a.H = p->H;
+            a.tw = p->tw;
+            a.tw_top = p->tw_top;
+            a.sync = reinterpret_cast<unsigned *>(scratch);
+            a.nsamples = nsamples;
+            a.stride = stride;
+            a.nblk = nblk;
+            a.nfull = nfull;
+            a.u0 = 0;
+            a.nu = 0;
+            a.nq = p->pair_nq;
+            a.lead = p->pair_lead;
+            a.M = (int)p->M;
+            a.L = (int)p->L;
+            a.nchan = (int)p->nchan;
+            e = launch_pair(a, p->pair_groups, s);
+        }
+        if (e == hipSuccess && nfull < nblk) {
+            const int groups = (int)(slots < p->max_groups ? slots : p->max_groups);
+            SplitArgs a;
+            a.x = (const float2 *)x_dev;
+            a.y = (float2 *)y_dev;
+            a.s0_old = p->state[p->parity];
+            a.s0_new = p->state[p->parity ^ 1];
+            a.H = p->H;
+            a.tw = p->tw;
+            a.tw_top = p->tw_top;
+            a.scratch = scratch + slot;
+            a.nsamples = nsamples;
+            a.stride = stride;
+            a.nblk = nblk;
+            a.blk0 = nfull;
+            a.M = (int)p->M;
+            a.L = (int)p->L;
+            a.nchan = (int)p->nchan;
+            e = launch_split(p->logn, a, groups, s, real);
+        }
     } else {
         FusedArgs a;
         a.x = (const float2 *)x_dev;

@@ -22,6 +22,9 @@ struct fir_ols_plan_s {
     float2 *tw_top = nullptr;     // W_N^{q k0} (split: full rows; multi-pass: two factors)
     float2 *scratch = nullptr;    // split: max_groups slots of N values; multi-pass: a batch of blocks
     int64_t scratch_elems = 0;    // float2 values at scratch
+    int pair_nq = 0;              // split path: work queues of the paired kernel (XCD ids)
+    int pair_groups = 0;          // split path: resident workgroups of the paired kernel
+    int pair_lead = 16;           // split path: producers handed out ahead of their consumers
     // host-resident streaming (fir_ols_execute_host), created on first use
     int64_t hs_chunk = 0;                      // samples per channel of a staging slot
     float2 *hs_x[2] = {nullptr, nullptr};      // device input slots [nchan][hs_chunk]

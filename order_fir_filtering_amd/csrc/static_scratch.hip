@@ -19,9 +19,9 @@
 
 namespace {
 
-// 64 MiB: 128 slots of the N = 65536 split path (one per workgroup, so at
-// most 128 workgroups run), or the blocks of one multi-pass batch
-// (8 blocks at N = 2^20, 64 at N = 2^17).
+// 64 MiB: at N = 65536 the two-workgroup kernel's flags (512 KB) and 127
+// slots for the one-workgroup kernel of partial last blocks; above 65536
+// the blocks of one multi-pass batch (8 blocks at N = 2^20, 64 at 2^17).
 constexpr int64_t kStaticScratchBytes = (int64_t)64 << 20;
 constexpr int64_t kStaticScratchElems = kStaticScratchBytes / (int64_t)sizeof(float2);
 constexpr int kMaxDevices = 64;

@@ -193,3 +193,36 @@ def test_large_multichannel_padded_stride_streaming(N, M):
     check(y[:, idx], ref, h, x, s0, f"N={N} {nchan} channels, stride {stride}")
     for c in range(nchan):
         np.testing.assert_array_equal(st[c], oracle.state_next(x[c], s0[c], M))
+
+
+@pytest.mark.parametrize("queues", ["16", "1"])
+def test_paired_kernel_queue_counts_are_bitwise_equal(queues, monkeypatch):
+    """The N = 65536 paired kernel with its work in more queues than the
+    GPU has XCDs (the last workgroup runs the unserved ones alone) or in one
+    queue: the same outputs and state, bit for bit, as with one queue per
+    XCD; and the oracle bound on sampled outputs."""
+    say(f"paired kernel, FIROLS_PAIR_QUEUES={queues}")
+    M, N = 16385, 65536
+    rng = np.random.default_rng(int(queues))
+    h = W.complex_taps(rng, M).astype(np.complex64)
+    L = N - M + 1
+    n = 37 * L + 1000
+    x = W.complex_normal(rng, (2, n))
+    s0 = W.complex_normal(rng, (2, M - 1))
+    H = W.freq_response_input(h, N)
+    with fo.Plan(M, N, 2) as pa:
+        pa.set_freq_response(H)
+        ya = run_calls(pa, x, [n], s0=s0)
+        sa = pa.get_state().cpu().numpy()
+    monkeypatch.setenv("FIROLS_PAIR_QUEUES", queues)
+    with fo.Plan(M, N, 2) as pb:
+        pb.set_freq_response(H)
+        yb = run_calls(pb, x, [n], s0=s0)
+        sb = pb.get_state().cpu().numpy()
+    monkeypatch.delenv("FIROLS_PAIR_QUEUES")
+    np.testing.assert_array_equal(yb, ya)
+    np.testing.assert_array_equal(sb, sa)
+    idx = np.unique(np.concatenate([np.arange(3000), W.sample_indices(5, n, 3000),
+                                    np.arange(n - 2000, n)]))
+    ref = oracle.fir_direct_multi(h, x, s0, idx=idx, threads=THREADS)
+    check(yb[:, idx], ref, h, x, s0, f"queues={queues}")
