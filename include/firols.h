@@ -80,9 +80,10 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan);
 
 /*
  * Set the filter from its taps (claim 1, step 1, first case): the taps are
- * zero-padded to N and transformed, on the GPU for N <= 32768 and on the
- * host in float64 for N >= 65536; H is kept scaled by 1/N so the inverse
- * transform of step 4 needs no separate scaling.
+ * zero-padded to N and transformed on the GPU (for N >= 65536 a radix-N/32768
+ * decimation with float64 phases, then 32768-point transforms); H is kept
+ * scaled by 1/N so the inverse transform of step 4 needs no separate
+ * scaling.
  *   h_host      host array: M float32 taps (is_complex == 0) or M
  *               interleaved complex64 taps (is_complex != 0); copied
  *               before return, the caller keeps ownership.

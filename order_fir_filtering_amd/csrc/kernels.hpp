@@ -45,6 +45,10 @@ hipError_t launch_big_plan_taps(const float2 *taps_padded, float2 *H, const floa
 // Split path (N = 65536): radix of the split (N / 32768; 1 when
 // N <= 2^kBigLogN), twiddle tables, H order, workgroups, launches.
 int split_radix(int logn);
+// H of a plan with N = 2^logn >= 65536 from N zero-padded complex taps, in
+// the split / multi-pass order (scaled by 1/N).
+hipError_t launch_split_plan_taps(int logn, const float2 *taps_padded, float2 *H,
+                                  const float2 *tw, hipStream_t stream);
 int split_sub_twiddle_count();
 int64_t split_top_twiddle_count(int logn);
 void build_split_twiddles(int logn, float2 *sub_tw, float2 *top_tw);

@@ -280,6 +280,84 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
     }
 }
 
+// Frequency response for N = RT * Ns >= 65536 (claim 1, step 1: the N-point
+// DFT of the zero-padded taps), in the order the split and multi-pass
+// kernels read it: H[k0 Ns + i] = DFT_N(taps)[k0 + RT k'] / N, where k' is
+// the bin that the Ns-point transform's digit-reversed order puts at
+// position i.  Workgroup k0 (RT of them) forms the decimated sequence
+//   a_k0[q] = sum_j taps[q + j Ns] W_N^{(q + j Ns) k0},  q < Ns,
+// so that DFT_N(taps)[k0 + RT k'] = DFT_Ns(a_k0)[k'], with the phases in
+// float64 (the exponent reduced mod N exactly) and the sum rounded to
+// float32 once; then the forward half of the Ns-point transform of
+// ols_big.hpp, as ols_big_plan_taps_kernel runs it for N = Ns.
+__global__ __launch_bounds__(kBig.TB) void ols_split_plan_taps_kernel(
+    const float2 *__restrict__ taps, float2 *__restrict__ H, const float2 *__restrict__ tw,
+    int lrt) {
+    __shared__ float2 lds[kHalfSlots];
+    const int tb = threadIdx.x;
+    const int k0 = blockIdx.x;
+    const int RT = 1 << lrt;
+    const int64_t N = (int64_t)kNs << lrt;
+    const TwTable<kBigGid> twt{tw, tb};
+    float2 a[kBig.P];
+    static_for<0, kBig.P>([&](auto Rr) {
+        constexpr int r = decltype(Rr)::value;
+        const int q = tb + kBig.TB * pass0_m<kBigGid>(r);
+        double re = 0.0, im = 0.0;
+        for (int j = 0; j < RT; ++j) {
+            const int64_t n = q + (int64_t)j * kNs;
+            const float2 h = taps[n];
+            // W_N^{n k0} = exp(-2 pi i e / N), e = n k0 mod N
+            const int64_t e = (n * k0) & (N - 1);
+            double sn, cs;
+            sincospi(-2.0 * (double)e / (double)N, &sn, &cs);
+            re += (double)h.x * cs - (double)h.y * sn;
+            im += (double)h.x * sn + (double)h.y * cs;
+        }
+        a[r] = make_float2((float)re, (float)im);
+    });
+    float2 rw[5];
+    load_pass0_rows<0>(rw, twt);
+    fwd_pass0_first<0>(a, rw);
+    put0<0, 0>(tb, a, lds);
+    pass0_twiddles<0, 16, 32, false>(a, rw);
+    load_pass0_rows<1>(rw, twt);
+    fwd_pass0_first<1>(a, rw);
+    put0<1, 0>(tb, a, lds);
+    pass0_twiddles<1, 16, 32, false>(a, rw);
+    const float scale = 1.0f / (float)N;   // exact: N is a power of two
+    float2 *__restrict__ Hk = H + (int64_t)k0 * kNs;
+    static_for<0, 2>([&](auto Hh) {
+        constexpr int h = decltype(Hh)::value;
+        if constexpr (h == 1) {
+            __syncthreads();
+            put0<0, 1>(tb, a, lds);
+            put0<1, 1>(tb, a, lds);
+        }
+        __syncthreads();
+        float2 c[32];
+        get_run<33>(lds + slot1(tb), c);
+        fwd_vt<1, h>(c, twt);
+        put_run<33>(lds + slot1(tb), c);
+        __syncthreads();
+        get_run<1>(lds + slot2(tb), c);
+        fwd_vt<2, h>(c, twt);
+        static_for<0, 32>([&](auto Kk) {
+            constexpr int k = decltype(Kk)::value;
+            Hk[(32 * h + k) * kBig.TB + tb] = make_float2(c[k].x * scale, c[k].y * scale);
+        });
+    });
+}
+
+hipError_t launch_split_plan_taps(int logn, const float2 *taps_padded, float2 *H,
+                                  const float2 *tw, hipStream_t stream) {
+    const int lrt = logn - kBig.logn;
+    if (lrt < 1 || lrt > kMaxLogN - kBig.logn) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(ols_split_plan_taps_kernel, dim3(1u << lrt), dim3(kBig.TB), 0, stream,
+                       taps_padded, H, tw, lrt);
+    return hipGetLastError();
+}
+
 int split_radix(int logn) { return logn > kBigLogN ? 1 << (logn - kBig.logn) : 1; }
 
 int split_sub_twiddle_count() { return twiddle_count(kBigGid); }

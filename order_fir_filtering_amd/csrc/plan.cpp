@@ -5,8 +5,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <cmath>
-#include <complex>
 #include <cstdint>
 #include <new>
 #include <utility>
@@ -48,36 +46,11 @@ int64_t state_len(const fir_ols_plan_s *p) { return p->nchan * (p->M - 1); }
 bool is_multi(const fir_ols_plan_s *p) { return p->logn > firols::kSplitLogN; }
 bool is_split(const fir_ols_plan_s *p) { return p->logn == firols::kSplitLogN; }
 bool is_big(const fir_ols_plan_s *p) { return p->logn == firols::kBigLogN; }
-// split and multi-pass paths: H from the host, in the split order
+// split and multi-pass paths: H in the split order
 bool host_response(const fir_ols_plan_s *p) { return p->logn > firols::kBigLogN; }
 // geometry id of the plan's table builders (fused and half-resident paths)
 int table_geometry(const fir_ols_plan_s *p) {
     return is_big(p) ? firols::big_geometry() : firols::fused_geometry(p->logn);
-}
-
-// In-place radix-2 DFT X[q] = sum_m x[m] e^{-2 pi i q m / N} in float64 (the
-// split path's frequency response, claim 1 step 1: the N-point FFT of the
-// zero-padded taps).  Iterative Cooley-Tukey: bit-reversal permutation, then
-// log2 N butterfly stages with twiddles from std::polar per stage.
-void host_fft(std::vector<std::complex<double>> &a) {
-    const size_t n = a.size();
-    for (size_t i = 1, j = 0; i < n; ++i) {
-        size_t bit = n >> 1;
-        for (; j & bit; bit >>= 1) j ^= bit;
-        j ^= bit;
-        if (i < j) std::swap(a[i], a[j]);
-    }
-    for (size_t len = 2; len <= n; len <<= 1) {
-        const size_t half = len >> 1;
-        std::vector<std::complex<double>> w(half);
-        for (size_t k = 0; k < half; ++k) w[k] = std::polar(1.0, -2.0 * M_PI * (double)k / (double)len);
-        for (size_t i = 0; i < n; i += len)
-            for (size_t k = 0; k < half; ++k) {
-                const std::complex<double> u = a[i + k], v = a[i + k + half] * w[k];
-                a[i + k] = u + v;
-                a[i + k + half] = u - v;
-            }
-    }
 }
 
 int upload_freq_response(fir_ols_plan_t p, const float *H_host, hipStream_t s);
@@ -177,23 +150,6 @@ int fir_ols_set_taps(fir_ols_plan_t p, const float *h_host, int64_t M, int is_co
                      void *stream) {
     if (!p || !h_host || M != p->M) return FIR_OLS_ERR_INVALID_ARG;
     if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
-    if (host_response(p)) {
-        // N >= 65536: H is computed on the host (float64) and takes the
-        // frequency-response path; no planning kernel runs for these sizes
-        std::vector<std::complex<double>> a((size_t)p->N, 0.0);
-        for (int64_t m = 0; m < M; ++m)
-            a[m] = is_complex ? std::complex<double>(h_host[2 * m], h_host[2 * m + 1])
-                              : std::complex<double>(h_host[m], 0.0);
-        host_fft(a);
-        std::vector<float> H((size_t)(2 * p->N));
-        for (int64_t q = 0; q < p->N; ++q) {
-            H[2 * q] = (float)a[q].real();
-            H[2 * q + 1] = (float)a[q].imag();
-        }
-        const int st = upload_freq_response(p, H.data(), (hipStream_t)stream);
-        if (st == FIR_OLS_OK) p->real_filter = !is_complex;
-        return st;
-    }
     std::vector<float2> padded((size_t)p->N, make_float2(0.f, 0.f));
     for (int64_t m = 0; m < M; ++m)
         padded[m] = is_complex ? make_float2(h_host[2 * m], h_host[2 * m + 1])
@@ -202,8 +158,9 @@ int fir_ols_set_taps(fir_ols_plan_t p, const float *h_host, int64_t M, int is_co
     hipError_t e = hipMemcpyAsync(p->taps, padded.data(), p->N * sizeof(float2),
                                   hipMemcpyHostToDevice, s);
     if (e == hipSuccess)
-        e = is_big(p) ? firols::launch_big_plan_taps(p->taps, p->H, p->tw, s)
-                      : firols::launch_plan_taps(p->logn, p->taps, p->H, p->tw, s);
+        e = host_response(p) ? firols::launch_split_plan_taps(p->logn, p->taps, p->H, p->tw, s)
+            : is_big(p)      ? firols::launch_big_plan_taps(p->taps, p->H, p->tw, s)
+                             : firols::launch_plan_taps(p->logn, p->taps, p->H, p->tw, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return FIR_OLS_ERR_HIP;
     p->has_filter = true;

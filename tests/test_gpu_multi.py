@@ -185,3 +185,26 @@ def test_multi_multichannel_padded_stride_streaming():
     check(y[:, idx], ref, h, x, s0, f"N={N} {nchan} channels, stride {stride}")
     for c in range(nchan):
         np.testing.assert_array_equal(st[c], oracle.state_next(x[c], s0[c], M))
+
+
+@pytest.mark.parametrize("N,M,d", [(1 << 16, 16385, 9001), (1 << 17, 40000, 31337),
+                                   (1 << 20, 262145, 200003)])
+def test_gpu_planner_delay_taps_shift_exactly(N, M, d):
+    """fir_ols_set_taps at N >= 65536 (the GPU frequency-response kernel):
+    taps that are one unit impulse at d give the input delayed by d, to
+    the rounding of the two transforms (claim 1, step 1: H is the DFT of the
+    padded taps)."""
+    say(f"planner, delay taps: N={N} M={M} d={d}")
+    rng = np.random.default_rng(N + d)
+    h = np.zeros(M, np.float32)
+    h[d] = 1.0
+    L = N - M + 1
+    n = 2 * L + 777
+    x = W.complex_normal(rng, (1, n))
+    s0 = W.complex_normal(rng, (1, M - 1))
+    with fo.Plan(M, N) as p:
+        p.set_taps(h)
+        y = run_calls(p, x, [n], s0=s0)
+    xt = np.concatenate([s0[0], x[0]])
+    want = xt[M - 1 - d: M - 1 - d + n]
+    check(y, want.astype(np.complex128), np.ones(1), x, s0, "delay taps")
