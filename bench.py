@@ -111,22 +111,43 @@ def _file_tag(kernel: str) -> str:
 
 
 def summarize_trace(args):
-    """profiles/<kernel>_<workload>_kernel_trace.md from run_kernel_stats.csv."""
+    """profiles/<kernel>_<workload>_kernel_trace.md from run_kernel_stats.csv:
+    one summary per configuration whose filtering kernel the run launched
+    (the default bench run launches all of them: the table and the
+    headline), each listing that kernel's calls and durations."""
+    import workloads as W
     rows = _csv_rows(args.summarize_trace, "kernel_stats.csv")
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    top = _file_tag(_short(rows[0]["Name"]))
-    out = os.path.join(PROFILES_DIR, f"{top}_{args.workload}_kernel_trace.md")
-    lines = [f"# Kernel trace: {args.workload} ({WORKLOAD_NOTE.get(args.workload, '')})", "",
-             "Command (working directory /tmp):", "", "```", args.command, "```", "",
-             f"Kernel source hash: `{kernel_source_hash(args.workload)}`", "",
-             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
-             "|---|---|---|---|---|---|"]
-    for r in rows[:8]:
-        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.3f} | "
-                     f"{float(r['MinNs'])/1e3:.3f} | {float(r['MaxNs'])/1e3:.3f} | "
-                     f"{float(r['Percentage']):.1f}% |")
-    open(out, "w").write("\n".join(lines) + "\n")
-    print(out)
+    by_name = {_short(r["Name"]).split("::")[-1]: r for r in rows}
+    keys = [args.workload] if args.workload in W.PFB_WORKLOADS else list(TABLE_KEYS)
+    written = []
+    for key in keys:
+        if key in W.PFB_WORKLOADS:
+            r = rows[0]
+        else:
+            kern = roofline_kernel(W.WORKLOADS[key].N)
+            r = by_name.get(kern)
+            if r is None:
+                continue
+        name = _short(r["Name"])
+        out = os.path.join(PROFILES_DIR, f"{_file_tag(name)}_{key}_kernel_trace.md")
+        lines = [f"# Kernel trace: {key} ({WORKLOAD_NOTE.get(key, '')})", "",
+                 "Command (working directory /tmp):", "", "```", args.command, "```", "",
+                 f"Kernel source hash: `{kernel_source_hash(key)}`", "",
+                 "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+                 "|---|---|---|---|---|---|",
+                 f"| `{name}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.3f} | "
+                 f"{float(r['MinNs'])/1e3:.3f} | {float(r['MaxNs'])/1e3:.3f} | "
+                 f"{float(r['Percentage']):.1f}% |", "",
+                 "Other kernels of the same run (top 8 by GPU time):", "",
+                 "| kernel | calls | average (us) | share of GPU time |", "|---|---|---|---|"]
+        for o in rows[:8]:
+            lines.append(f"| `{_short(o['Name'])}` | {o['Calls']} | "
+                         f"{float(o['AverageNs'])/1e3:.3f} | {float(o['Percentage']):.1f}% |")
+        open(out, "w").write("\n".join(lines) + "\n")
+        written.append(out)
+    for w in written:
+        print(w)
 
 
 def summarize_pmc(args):
