@@ -99,4 +99,54 @@ constexpr int last_pass_position(const Geo &g, int tb, int r) {
     return v * R + k;
 }
 
+// Position held by register r of thread tb in the layout of pass s (r =
+// u * R[s] + j for virtual thread u, see above).
+constexpr int layout_position(const Geo &g, int s, int tb, int r) {
+    const int R = g.R[s], S = g.S[s];
+    const int v = tb + g.TB * (r / R);
+    return (v / S) * S * R + v % S + S * (r % R);
+}
+
+// Exchange between the layouts of two passes done inside the registers of
+// a wave: register bit rb[i] of every thread is swapped with bit 4 + i of
+// its lane (rb[i] < 0: that lane bit keeps its position bit).  Swapping
+// register bit b with lane bit 4 (5) is one exchange of 16-lane (32-lane)
+// rows between each pair of registers that differ in bit b.  `ok` is set
+// only when every register of every thread of the block lands on the
+// position the target layout assigns to it, and the block fills whole
+// 32-lane halves or whole waves (TB = 32 or 64, lanes = tb).
+struct LaneSwap {
+    bool ok;
+    int rb[2];
+};
+constexpr LaneSwap lane_swap_plan(const Geo &g, int from, int to) {
+    LaneSwap ls{false, {-1, -1}};
+    if (g.TB != 32 && g.TB != 64) return ls;
+    for (int i = 0; i < 2; ++i) {
+        const int lb = 4 + i;
+        if ((1 << lb) >= g.TB) continue;
+        // the position bit that lane bit lb carries in the source layout
+        const int e = layout_position(g, from, 1 << lb, 0) - layout_position(g, from, 0, 0);
+        for (int rb = 0; (1 << rb) < g.P; ++rb)
+            if (layout_position(g, to, 0, 1 << rb) - layout_position(g, to, 0, 0) == e)
+                ls.rb[i] = rb;
+    }
+    if (ls.rb[0] < 0 && ls.rb[1] < 0) return ls;
+    if (ls.rb[0] == ls.rb[1]) return ls;
+    for (int tb = 0; tb < g.TB; ++tb)
+        for (int r = 0; r < g.P; ++r) {
+            int sr = r, st = tb;   // where the value of (tb, r) comes from
+            for (int i = 0; i < 2; ++i) {
+                const int rb = ls.rb[i], lb = 4 + i;
+                if (rb < 0) continue;
+                const int c = (r >> rb) & 1, l = (tb >> lb) & 1;
+                sr = (sr & ~(1 << rb)) | (l << rb);
+                st = (st & ~(1 << lb)) | (c << lb);
+            }
+            if (layout_position(g, from, st, sr) != layout_position(g, to, tb, r)) return ls;
+        }
+    ls.ok = true;
+    return ls;
+}
+
 }  // namespace firols

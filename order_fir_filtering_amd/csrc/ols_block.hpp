@@ -45,7 +45,54 @@ __device__ __forceinline__ void exchange_sync() {
         __syncthreads();
 }
 
-// Forward passes with LDS exchanges between them.
+// Swap one float between two registers across lane bit LB (4: the odd
+// 16-lane rows of `lo` with the even rows of `hi`; 5: the upper 32 lanes of
+// `lo` with the lower 32 lanes of `hi`).  Afterwards `lo` holds, at a lane
+// with bit LB clear, its own old value and at a lane with bit LB set the
+// old `hi` of the lane with that bit clear; `hi` the converse.
+template <int LB>
+__device__ __forceinline__ void row_swap(float &lo, float &hi) {
+    const unsigned x = __builtin_bit_cast(unsigned, lo), y = __builtin_bit_cast(unsigned, hi);
+    if constexpr (LB == 4) {
+        const auto v = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+        lo = __builtin_bit_cast(float, (unsigned)v[0]);
+        hi = __builtin_bit_cast(float, (unsigned)v[1]);
+    } else {
+        static_assert(LB == 5, "row swaps exist for lane bits 4 and 5");
+        const auto v = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+        lo = __builtin_bit_cast(float, (unsigned)v[0]);
+        hi = __builtin_bit_cast(float, (unsigned)v[1]);
+    }
+}
+
+// Exchange from the layout of pass FROM to that of pass TO inside the
+// wave's registers, when lane_swap_plan accepts it: for N = 1024 (radices
+// 4, 16, 16, one wave per block) the exchange between the first two passes
+// moves position bits 8, 9 from registers to lanes 4, 5 and bits 4, 5 the
+// other way, i.e. two row swaps per pair of registers and no LDS round
+// trip or barrier; N = 512 needs one.
+template <int GID, int FROM, int TO>
+__device__ __forceinline__ void lane_exchange(float2 (&a)[make_geo(GID).P]) {
+    constexpr Geo G = make_geo(GID);
+    constexpr LaneSwap ls = lane_swap_plan(G, FROM, TO);
+    static_assert(ls.ok, "exchange is not a set of lane-row swaps");
+    static_for<0, 2>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        constexpr int rb = ls.rb[i];
+        if constexpr (rb >= 0) {
+            static_for<0, G.P>([&](auto Rr) {
+                constexpr int r = decltype(Rr)::value;
+                if constexpr ((r & (1 << rb)) == 0) {
+                    row_swap<4 + i>(a[r].x, a[r | (1 << rb)].x);
+                    row_swap<4 + i>(a[r].y, a[r | (1 << rb)].y);
+                }
+            });
+        }
+    });
+}
+
+// Forward passes with exchanges between them: inside the wave's registers
+// where the layouts allow it (lane_exchange), else through LDS.
 template <int GID, class TW>
 __device__ __forceinline__ void forward_all(int tb, float2 (&a)[make_geo(GID).P],
                                             float2 *lds, const TW &tw) {
@@ -53,16 +100,20 @@ __device__ __forceinline__ void forward_all(int tb, float2 (&a)[make_geo(GID).P]
     static_for<0, G.npass>([&](auto Sx) {
         constexpr int s = decltype(Sx)::value;
         if constexpr (s > 0) {
-            block_sync<GID>();
-            lds_put<GID, s - 1>(tb, a, lds);
-            exchange_sync<GID, s>();
-            lds_get<GID, s>(tb, a, lds);
+            if constexpr (lane_swap_plan(G, s - 1, s).ok) {
+                lane_exchange<GID, s - 1, s>(a);
+            } else {
+                block_sync<GID>();
+                lds_put<GID, s - 1>(tb, a, lds);
+                exchange_sync<GID, s>();
+                lds_get<GID, s>(tb, a, lds);
+            }
         }
         fwd_pass<GID, s>(a, tw);
     });
 }
 
-// Inverse passes in reverse order with LDS exchanges between them.
+// Inverse passes in reverse order, exchanged as in forward_all.
 template <int GID, class TW>
 __device__ __forceinline__ void inverse_all(int tb, float2 (&a)[make_geo(GID).P],
                                             float2 *lds, const TW &tw) {
@@ -70,10 +121,14 @@ __device__ __forceinline__ void inverse_all(int tb, float2 (&a)[make_geo(GID).P]
     static_for<0, G.npass>([&](auto Ix) {
         constexpr int s = G.npass - 1 - decltype(Ix)::value;
         if constexpr (s < G.npass - 1) {
-            block_sync<GID>();
-            lds_put<GID, s + 1>(tb, a, lds);
-            exchange_sync<GID, s + 1>();
-            lds_get<GID, s>(tb, a, lds);
+            if constexpr (lane_swap_plan(G, s + 1, s).ok) {
+                lane_exchange<GID, s + 1, s>(a);
+            } else {
+                block_sync<GID>();
+                lds_put<GID, s + 1>(tb, a, lds);
+                exchange_sync<GID, s + 1>();
+                lds_get<GID, s>(tb, a, lds);
+            }
         }
         inv_pass<GID, s>(a, tw);
     });
@@ -107,8 +162,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uin
                                              0x00020000);
 }
 // Non-temporal load (cache-policy bit 1): for input that the small-block
-// kernel streams through once; the M-1 samples two neighbouring blocks
-// share are read by workgroups running side by side.
+// kernel streams through once when every workgroup has a single block
+// (several blocks per workgroup measured faster with the default policy,
+// which keeps the M-1 samples two neighbouring blocks share in L2 longer).
 __device__ __forceinline__ float2 buf_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 2));
 }

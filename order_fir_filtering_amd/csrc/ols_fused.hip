@@ -164,15 +164,19 @@ __global__ __launch_bounds__(FusedCfg<GID>::WG, FusedCfg<GID>::MIN_WAVES_PER_SIM
         // loads are in flight while the transform runs (a and b alternate;
         // the transform itself issues no memory loads).  Measured on 1024
         // channels at N = 1024: 290 -> 303 GS/s; one long call at N = 2048:
-        // 245 -> 268 GS/s.
+        // 245 -> 268 GS/s.  These loads take the default cache policy: the
+        // M-1 samples a block shares with the next one are then found in L2
+        // more often when a neighbouring wave reads them (1024 channels at
+        // N = 1024: 306 -> 315 GS/s against the non-temporal policy, which
+        // the one-block-per-workgroup case keeps).
         float2 b[G.P];
         for (int64_t it = 1; unit >= 0; it += 2) {
             const int64_t u1 = unit_of(units, blockIdx.x, gridDim.x, it);
-            if (u1 >= 0) gather_block_wave<GID, false, true, 0, G.P, REAL>(A, u1 * C::BPW + sub, tb, b);
+            if (u1 >= 0) gather_block_wave<GID, false, false, 0, G.P, REAL>(A, u1 * C::BPW + sub, tb, b);
             process_block_wave<GID, REAL>(A, unit * C::BPW + sub, tb, a, my, tw, hp);
             if (u1 < 0) break;
             const int64_t u2 = unit_of(units, blockIdx.x, gridDim.x, it + 1);
-            if (u2 >= 0) gather_block_wave<GID, false, true, 0, G.P, REAL>(A, u2 * C::BPW + sub, tb, a);
+            if (u2 >= 0) gather_block_wave<GID, false, false, 0, G.P, REAL>(A, u2 * C::BPW + sub, tb, a);
             process_block_wave<GID, REAL>(A, u1 * C::BPW + sub, tb, b, my, tw, hp);
             unit = u2;
         }

@@ -16,7 +16,7 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 import workloads as W  # noqa: E402
 
-KERN = "firols::ols_fused_kernel<12>(firols::FusedArgs)"
+KERN = "void firols::ols_fused_kernel<12, false>(firols::FusedArgs)"
 COPY = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>(int)"
 
 
@@ -68,7 +68,7 @@ def test_valu_summary_and_line(tmp_path, monkeypatch):
     assert rec["fp32_flops_per_sample"] == pytest.approx(want / samples, abs=0.01)
     assert rec["valu_instr_per_sample"] == pytest.approx(64 * instr / samples, abs=0.01)
     assert rec["source_hash"] == bench.kernel_source_hash("cfg2")
-    assert (prof / "ols_fused_kernel_12_cfg2_valu.md").exists()
+    assert (prof / "ols_fused_kernel_12_false_cfg2_valu.md").exists()
 
     monkeypatch.setattr(bench, "PROFILES_DIR", str(prof))
     line = bench.valu_line("cfg2", 0.01)            # 10 us per launch
@@ -115,5 +115,5 @@ def test_trace_summary_names_the_top_kernel(tmp_path, monkeypatch):
     prof.mkdir()
     run_main(monkeypatch, ["--workload", "cfg2", "--summarize-trace", str(d),
                            "--profiles-dir", str(prof)])
-    text = open(prof / "ols_fused_kernel_12_cfg2_kernel_trace.md").read()
+    text = open(prof / "ols_fused_kernel_12_false_cfg2_kernel_trace.md").read()
     assert "| 400 | 9.000 |" in text

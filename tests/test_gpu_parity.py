@@ -271,3 +271,40 @@ def test_set_state_none_zeroes_and_m1_has_no_state():
         p.set_taps(np.array([2.0], np.float32))
         y = run_calls(p, x, [40, 60])
     check(y, 2.0 * x.astype(np.complex128), np.array([2.0]), x, None, "M=1")
+
+
+def _many_block_cases():
+    # (N, threads per block TB, blocks per channel, channels): enough blocks
+    # that every resident workgroup takes several, with L = N - M + 1 a
+    # multiple s*TB of the threads per block, so that the overlap of a block
+    # ends on each possible register row boundary
+    cases = []
+    for N, TB, nb, nchan in ((1024, 64, 131, 47), (2048, 128, 97, 31), (4096, 256, 211, 9)):
+        P = N // TB
+        for s in sorted({1, 2, P // 4, P // 2 + 1, 3 * P // 4, P - 1}):
+            cases.append((N, N - s * TB + 1, nb, nchan))
+    return cases
+
+
+@pytest.mark.parametrize("N,M,nb,nchan", _many_block_cases())
+def test_many_blocks_block_length_on_row_boundaries(N, M, nb, nchan):
+    """Many blocks per workgroup, each block's overlap (claim 1, step 3:
+    D_(i-1) in front of B_i) ending on every register row boundary: every
+    output and state against the oracle, over ragged channel lengths and
+    two calls."""
+    L = N - M + 1
+    n = nb * L - 17
+    say(f"row boundaries: N={N} M={M} L={L} blocks/ch={nb} nchan={nchan}")
+    rng = np.random.default_rng(N + M)
+    h = rng.standard_normal(M).astype(np.float32) / np.sqrt(M)
+    x = W.complex_normal(rng, (nchan, n))
+    s0 = W.complex_normal(rng, (nchan, M - 1))
+    calls = [n // 3 * 2 + 5, n - (n // 3 * 2 + 5)]
+    with fo.Plan(M, N, nchan) as p:
+        p.set_taps(h)
+        y = run_calls(p, x, calls, s0=s0)
+        st = p.get_state().cpu().numpy()
+    ref = oracle_multi(h, x, s0)
+    check(y, ref, h, x, s0, f"rows N={N} M={M}")
+    for c in range(nchan):
+        np.testing.assert_array_equal(st[c], oracle.state_next(x[c], s0[c], M))
