@@ -53,7 +53,8 @@ enum {
     FIR_OLS_ERR_ALIGN = -5,        /* device pointer not 8-byte aligned */
     FIR_OLS_ERR_OOM = -6,          /* device allocation failed */
     FIR_OLS_ERR_HIP = -7,          /* HIP runtime error (launch, copy, sync) */
-    FIR_OLS_ERR_DEVICE = -8        /* current device is not the plan's device */
+    FIR_OLS_ERR_DEVICE = -8,       /* current device is not the plan's device */
+    FIR_OLS_ERR_TIMEOUT = -9       /* a kernel's bounded wait ran out (fir_ols_check) */
 };
 
 /*
@@ -235,6 +236,22 @@ int fir_ols_set_state(fir_ols_plan_t p, const void *s0_dev, void *stream);
  * Stream-ordered and asynchronous.
  */
 int fir_ols_get_state(fir_ols_plan_t p, void *s0_out_dev, void *stream);
+
+/*
+ * Kernel-side errors of the calls enqueued so far.  For N = 65536 the
+ * second workgroup of a block waits, bounded to 0.5 s, for the first to
+ * park its half-spectrum (claim 1, step 4 split over two workgroups).  The
+ * launch order means the first is always running, so the bound is not
+ * reached in normal operation.  If it is, that wait gives up, the block's
+ * outputs are written as quiet NaN, and the plan's device error word is
+ * set.  fir_ols_check synchronizes `stream`, reads and clears that word,
+ * and returns FIR_OLS_ERR_TIMEOUT if it was set (FIR_OLS_OK otherwise, or
+ * FIR_OLS_ERR_HIP / FIR_OLS_ERR_DEVICE).  Calls through
+ * fir_ols_execute_static report through the same word.  The environment
+ * variable FIROLS_PAIR_HOLD_READY=1 at plan creation makes every such wait
+ * run out after 10 us (a test of this path; never set it otherwise).
+ */
+int fir_ols_check(fir_ols_plan_t p, void *stream);
 
 /*
  * Destroy a plan: waits for the plan's device to finish, then frees its

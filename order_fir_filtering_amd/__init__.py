@@ -25,8 +25,8 @@ __all__ = [
     "fir_ols_plan", "fir_ols_set_taps", "fir_ols_set_freq_response",
     "fir_ols_execute", "fir_ols_execute_host", "fir_ols_execute_real", "fir_ols_execute_static",
     "fir_ols_static_scratch_bytes", "fir_ols_set_state",
-    "fir_ols_get_state", "fir_ols_destroy", "fir_ols_block_length", "fir_ols_choose_n",
-    "fir_ols_status_string", "Channelizer", "fir_pfb_plan", "fir_pfb_set_taps",
+    "fir_ols_get_state", "fir_ols_check", "fir_ols_destroy", "fir_ols_block_length",
+    "fir_ols_choose_n", "fir_ols_status_string", "Channelizer", "fir_pfb_plan", "fir_pfb_set_taps",
     "fir_pfb_execute", "fir_pfb_set_state", "fir_pfb_get_state", "fir_pfb_destroy",
 ]
 
@@ -35,8 +35,8 @@ EXPORTED = (
     "fir_ols_plan", "fir_ols_set_taps", "fir_ols_set_freq_response",
     "fir_ols_execute", "fir_ols_execute_host", "fir_ols_execute_real", "fir_ols_execute_static",
     "fir_ols_static_scratch_bytes", "fir_ols_set_state",
-    "fir_ols_get_state", "fir_ols_destroy", "fir_ols_block_length", "fir_ols_choose_n",
-    "fir_ols_status_string", "fir_pfb_plan", "fir_pfb_set_taps", "fir_pfb_execute",
+    "fir_ols_get_state", "fir_ols_check", "fir_ols_destroy", "fir_ols_block_length",
+    "fir_ols_choose_n", "fir_ols_status_string", "fir_pfb_plan", "fir_pfb_set_taps", "fir_pfb_execute",
     "fir_pfb_set_state", "fir_pfb_get_state", "fir_pfb_destroy",
 )
 
@@ -44,6 +44,7 @@ STATUS = {
     0: "FIR_OLS_OK", -1: "FIR_OLS_ERR_INVALID_ARG", -2: "FIR_OLS_ERR_UNSUPPORTED",
     -3: "FIR_OLS_ERR_NO_FILTER", -4: "FIR_OLS_ERR_ALIAS", -5: "FIR_OLS_ERR_ALIGN",
     -6: "FIR_OLS_ERR_OOM", -7: "FIR_OLS_ERR_HIP", -8: "FIR_OLS_ERR_DEVICE",
+    -9: "FIR_OLS_ERR_TIMEOUT",
 }
 
 
@@ -81,6 +82,7 @@ def load_library(path: Optional[str] = None):
         "fir_ols_static_scratch_bytes": (_i64, []),
         "fir_ols_set_state": (_int, [_vp, _vp, _vp]),
         "fir_ols_get_state": (_int, [_vp, _vp, _vp]),
+        "fir_ols_check": (_int, [_vp, _vp]),
         "fir_ols_destroy": (_int, [_vp]),
         "fir_ols_block_length": (_i64, [_vp]),
         "fir_ols_choose_n": (_i64, [_i64]),
@@ -201,6 +203,13 @@ def fir_ols_get_state(plan: int, out, stream=None) -> None:
     _check(lib.fir_ols_get_state(plan, _ptr(out), _stream(stream)), "fir_ols_get_state")
 
 
+def fir_ols_check(plan: int, stream=None) -> None:
+    """Synchronize the stream and raise FirOlsError(FIR_OLS_ERR_TIMEOUT) if
+    a kernel wait of the plan's calls ran out (the word is then cleared)."""
+    lib = load_library()
+    _check(lib.fir_ols_check(plan, _stream(stream)), "fir_ols_check")
+
+
 def fir_ols_destroy(plan: Optional[int]) -> None:
     lib = load_library()
     _check(lib.fir_ols_destroy(plan), "fir_ols_destroy")
@@ -297,6 +306,9 @@ class Plan:
         out = torch.empty((self.nchan, self.M - 1), dtype=torch.complex64, device="cuda")
         fir_ols_get_state(self.handle, out, stream)
         return out
+
+    def check(self, stream=None) -> None:
+        fir_ols_check(self.handle, stream)
 
     def close(self) -> None:
         if getattr(self, "handle", None):

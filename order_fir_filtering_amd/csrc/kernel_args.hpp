@@ -54,6 +54,8 @@ struct PairArgs {
     const float2 *tw;       // twiddle table of the Ns-point sub-transform
     const float2 *tw_top;   // 2 * Ns values W_N^{q k0} (row 0 all ones)
     unsigned *sync;         // kPairSyncHeader words (queue heads, exit count), then nu flags
+    unsigned *err;          // the plan's error word: set to 1 when a consumer's wait times out
+    uint64_t wait_ticks;    // bound of a consumer's wait, 100 MHz constant-clock ticks
     int64_t nsamples;       // samples per channel in this call (> 0)
     int64_t stride;         // elements between channel starts
     int64_t nblk;           // blocks per channel
@@ -62,6 +64,7 @@ struct PairArgs {
     int nu;                 // units in the launch
     int nq;                 // work queues: one per XCD id 0 .. nq-1
     int lead;               // blocks whose producers a queue hands out before their consumers
+    int hold_ready;         // test switch: producers park c_0 but raise no flag
     int M;
     int L;
     int nchan;

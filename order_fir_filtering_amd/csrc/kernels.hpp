@@ -62,6 +62,8 @@ hipError_t launch_split(int logn, const SplitArgs &a, int max_groups, hipStream_
 // one call (a counter reset and the kernel per batch of units).
 int pair_queue_count(int device);
 int pair_lead();
+bool pair_hold_ready();
+uint64_t pair_wait_ticks(bool hold);
 int pair_max_groups(int device);
 hipError_t launch_pair(const PairArgs &a, int max_groups, hipStream_t stream);
 

@@ -51,6 +51,7 @@ namespace {
 
 constexpr int kNs = kBig.N;                      // points of a sub-transform
 constexpr uint64_t kReadyWaitTicks = 50000000;   // 0.5 s of the 100 MHz constant clock
+constexpr uint64_t kHeldWaitTicks = 1000;        // 10 us: the bound under FIROLS_PAIR_HOLD_READY
 constexpr int kPairLead = 16;                    // default lead (measured best of 1 .. 16)
 
 // XCD (XCC) the wave runs on: hardware register XCC_ID, bits 3:0.
@@ -138,6 +139,18 @@ __device__ __forceinline__ void pair_combine(const float2 (&a)[64], int qo, int 
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// What a consumer whose wait for c_0 timed out stores for virtual thread U
+// instead of pair_combine's values: a quiet NaN at every kept position.
+template <int U>
+__device__ __forceinline__ void pair_fill_nan(int qo, int fo, __amdgpu_buffer_rsrc_t ry) {
+    const float2 nan = make_float2(__builtin_nanf(""), __builtin_nanf(""));
+    static_for<0, 32>([&](auto Ii) {
+        constexpr int off = kBig.TB * pass0_m<kBigGid>(32 * U + decltype(Ii)::value);
+        buf_store(nan, ry, (uint32_t)(off + qo) * 8u);
+        buf_store(nan, ry, (uint32_t)(off + fo) * 8u);
+    });
+}
+
 // Block (c, i) of unit u, and the offset g0 of its first point in the
 // channel's input (negative: the state is in front).
 struct PairBlock {
@@ -223,24 +236,45 @@ __device__ __forceinline__ void pair_item(const PairArgs &A, int64_t u, unsigned
                       [](auto, float2(&)[64]) {});
         wait_vmem();
         __syncthreads();
-        if (tb == 0) __hip_atomic_store(ready, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tb == 0 && !A.hold_ready)
+            __hip_atomic_store(ready, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
         // consumer: wait for c_0 when the first virtual thread's c_1 is
-        // final, combine it while the transform finishes the second one
+        // final, combine it while the transform finishes the second one.
+        // The wait is bounded; when it runs out, the plan's error word is
+        // set and the block's outputs become NaN instead of a combine with
+        // whatever the output range holds.
+        __shared__ int sh_ok;
+        int ok = 1;
         big_transform(tb, a, r0, r1, lds, TwBig{rtw, lds_tw, tb}, rh,
                       [&](auto Uu, const float2(&v)[64]) {
                           constexpr int U = decltype(Uu)::value;
                           if constexpr (U == 0) {
                               if (tb == 0) {
                                   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-                                  while (__hip_atomic_load(ready, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT) == 0u &&
-                                         __builtin_amdgcn_s_memrealtime() - t0 < kReadyWaitTicks)
+                                  int got = 0;
+                                  for (;;) {
+                                      if (__hip_atomic_load(ready, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+                                          got = 1;
+                                          break;
+                                      }
+                                      if (__builtin_amdgcn_s_memrealtime() - t0 >= A.wait_ticks)
+                                          break;
                                       __builtin_amdgcn_s_sleep(2);
+                                  }
+                                  if (!got)
+                                      __hip_atomic_store(A.err, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+                                  sh_ok = got;
                               }
                               __syncthreads();
+                              ok = __builtin_amdgcn_readfirstlane(sh_ok);
                           }
-                          pair_combine<U>(v, qo, fo, ry, wt, wm);
+                          if (ok)
+                              pair_combine<U>(v, qo, fo, ry, wt, wm);
+                          else
+                              pair_fill_nan<U>(qo, fo, ry);
                       },
                       [](auto, float2(&)[64]) {});
         if (i == A.nblk - 1)
@@ -371,6 +405,17 @@ int pair_lead() {
     }
     return kPairLead;
 }
+
+bool pair_hold_ready() {
+    // FIROLS_PAIR_HOLD_READY=1 (read at plan creation) is a test switch:
+    // producers raise no flag and consumers wait kHeldWaitTicks, so every
+    // consumer's wait runs out and the error path can be exercised with
+    // every kernel still ending normally
+    const char *env = std::getenv("FIROLS_PAIR_HOLD_READY");
+    return env && std::atoi(env) == 1;
+}
+
+uint64_t pair_wait_ticks(bool hold) { return hold ? kHeldWaitTicks : kReadyWaitTicks; }
 
 int pair_max_groups(int device) {
     int cus = 0, per_cu = 0;

@@ -33,6 +33,7 @@ void release(fir_ols_plan_s *p) {
     release_host_stream(p);
     (void)hipFree(p->tw_top);
     (void)hipFree(p->scratch);
+    (void)hipFree(p->err);
     (void)hipFree(p->H);
     (void)hipFree(p->tw);
     (void)hipFree(p->taps);
@@ -100,13 +101,16 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
     if (split) {
         p->pair_nq = firols::pair_queue_count(p->device);
         p->pair_lead = firols::pair_lead();
+        p->pair_hold = firols::pair_hold_ready();
         p->pair_groups = firols::pair_max_groups(p->device);
         (void)hipGetLastError();
     }
     const size_t sbytes = (size_t)state_len(p) * sizeof(float2);
     bool ok = hipMalloc(&p->H, N * sizeof(float2)) == hipSuccess &&
               hipMalloc(&p->tw, (size_t)(ntw > 0 ? ntw : 1) * sizeof(float2)) == hipSuccess &&
-              hipMalloc(&p->taps, N * sizeof(float2)) == hipSuccess;
+              hipMalloc(&p->taps, N * sizeof(float2)) == hipSuccess &&
+              hipMalloc(&p->err, sizeof(unsigned)) == hipSuccess &&
+              hipMemset(p->err, 0, sizeof(unsigned)) == hipSuccess;
     if (ok && sbytes) {
         ok = hipMalloc(&p->state[0], sbytes) == hipSuccess &&
              hipMalloc(&p->state[1], sbytes) == hipSuccess;
@@ -282,6 +286,9 @@ int execute_with_scratch(fir_ols_plan_s *p, const void *x_dev, void *y_dev, int6
             a.nu = 0;
             a.nq = p->pair_nq;
             a.lead = p->pair_lead;
+            a.hold_ready = p->pair_hold ? 1 : 0;
+            a.err = p->err;
+            a.wait_ticks = firols::pair_wait_ticks(p->pair_hold);
             a.M = (int)p->M;
             a.L = (int)p->L;
             a.nchan = (int)p->nchan;
@@ -366,6 +373,20 @@ int fir_ols_get_state(fir_ols_plan_t p, void *s0_out_dev, void *stream) {
     return e == hipSuccess ? FIR_OLS_OK : FIR_OLS_ERR_HIP;
 }
 
+int fir_ols_check(fir_ols_plan_t p, void *stream) {
+    if (!p) return FIR_OLS_ERR_INVALID_ARG;
+    if (!on_plan_device(p)) return FIR_OLS_ERR_DEVICE;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return FIR_OLS_ERR_HIP;
+    unsigned h = 0;
+    if (hipMemcpy(&h, p->err, sizeof h, hipMemcpyDeviceToHost) != hipSuccess)
+        return FIR_OLS_ERR_HIP;
+    if (h == 0) return FIR_OLS_OK;
+    const unsigned zero = 0;
+    if (hipMemcpy(p->err, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess)
+        return FIR_OLS_ERR_HIP;
+    return FIR_OLS_ERR_TIMEOUT;
+}
+
 int fir_ols_destroy(fir_ols_plan_t p) {
     if (!p) return FIR_OLS_OK;
     const int dev = p->device;
@@ -417,6 +438,7 @@ const char *fir_ols_status_string(int status) {
         case FIR_OLS_ERR_OOM: return "device allocation failed";
         case FIR_OLS_ERR_HIP: return "HIP runtime error";
         case FIR_OLS_ERR_DEVICE: return "current device is not the plan's device";
+        case FIR_OLS_ERR_TIMEOUT: return "a kernel's wait for another workgroup ran out";
         default: return "unknown status";
     }
 }

@@ -226,3 +226,47 @@ def test_paired_kernel_queue_counts_are_bitwise_equal(queues, monkeypatch):
                                     np.arange(n - 2000, n)]))
     ref = oracle.fir_direct_multi(h, x, s0, idx=idx, threads=THREADS)
     check(yb[:, idx], ref, h, x, s0, f"queues={queues}")
+
+
+def test_paired_wait_timeout_reports_error(monkeypatch):
+    """A consumer whose bounded wait for the producer's parked half-spectrum
+    runs out.  The timeout is forced from the host: with
+    FIROLS_PAIR_HOLD_READY=1 at plan creation the producers raise no flag
+    and the bound is 10 us, so every kernel still ends normally.
+    fir_ols_check reports FIR_OLS_ERR_TIMEOUT once and clears it.  The full
+    blocks' outputs are NaN, not a combine with stale data.  The partial
+    last block (the one-workgroup kernel, which waits for nothing) and the
+    state are still right.  A plan made without the switch is unaffected."""
+    M, N = 16385, 65536
+    L = N - M + 1
+    n = 3 * L + 1000
+    rng = np.random.default_rng(41)
+    h = W.complex_taps(rng, M).astype(np.complex64)
+    x = W.complex_normal(rng, (1, n))
+    s0 = W.complex_normal(rng, (1, M - 1))
+    H = W.freq_response_input(h, N)
+    say("paired kernel, FIROLS_PAIR_HOLD_READY=1 (every consumer's wait runs out)")
+    monkeypatch.setenv("FIROLS_PAIR_HOLD_READY", "1")
+    with fo.Plan(M, N, 1) as p:
+        monkeypatch.delenv("FIROLS_PAIR_HOLD_READY")
+        p.set_freq_response(H)
+        y = run_calls(p, x, [n], s0=s0)
+        with pytest.raises(fo.FirOlsError) as err:
+            p.check()
+        assert err.value.status == -9
+        p.check()   # the word was cleared
+        st = p.get_state().cpu().numpy()
+    assert np.isnan(y[0, :3 * L].real).all() and np.isnan(y[0, :3 * L].imag).all()
+    tail = np.arange(3 * L, n)
+    ref = oracle.fir_direct_multi(h, x, s0, idx=tail, threads=THREADS)
+    check(y[:, tail], ref, h, x, s0, "partial last block after the timeouts")
+    np.testing.assert_array_equal(st[0], oracle.state_next(x[0], s0[0], M))
+
+    with fo.Plan(M, N, 1) as q:
+        q.set_freq_response(H)
+        y2 = run_calls(q, x, [n], s0=s0)
+        q.check()
+    idx = np.unique(np.concatenate([np.arange(2000), W.sample_indices(9, n, 3000),
+                                    np.arange(n - 2000, n)]))
+    ref = oracle.fir_direct_multi(h, x, s0, idx=idx, threads=THREADS)
+    check(y2[:, idx], ref, h, x, s0, "plan without the switch")
