@@ -52,7 +52,7 @@ namespace {
 constexpr int kNs = kBig.N;                      // points of a sub-transform
 constexpr uint64_t kReadyWaitTicks = 50000000;   // 0.5 s of the 100 MHz constant clock
 constexpr uint64_t kHeldWaitTicks = 1000;        // 10 us: the bound under FIROLS_PAIR_HOLD_READY
-constexpr int kPairLead = 16;                    // default lead (measured best of 1 .. 16)
+constexpr int kPairLead = 9;                     // default lead (measured best of 1 .. 64)
 
 // XCD (XCC) the wave runs on: hardware register XCC_ID, bits 3:0.
 __device__ __forceinline__ int xcc_id() {
@@ -74,8 +74,11 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // E[q + j Ns] through load(j, q - tb); W_N^q = W_N^tb W_N^{TB m}, the
 // second factor from the LDS table wm.  The loads are software-pipelined:
 // kGatherAhead point pairs are in flight, and each pair consumed requests
-// the next one.
-constexpr int kGatherAhead = 28;
+// the next one.  A shallow pipeline is enough: the gathers of many
+// workgroups at once load the memory system, not one CU's latency (on the
+// 65536-point workload 28 pairs: 1.99 ms per call, 12: 1.96, 8 and 4:
+// 1.956), and it leaves the compiler registers (fewer spills).
+constexpr int kGatherAhead = 8;
 template <bool HALF1, class LOAD>
 __device__ __forceinline__ void pair_gather(float2 (&a)[64], const LOAD &load, float2 wt,
                                             const float2 *wm) {
