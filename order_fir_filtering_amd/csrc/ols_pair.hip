@@ -52,7 +52,7 @@ namespace {
 constexpr int kNs = kBig.N;                      // points of a sub-transform
 constexpr uint64_t kReadyWaitTicks = 50000000;   // 0.5 s of the 100 MHz constant clock
 constexpr uint64_t kHeldWaitTicks = 1000;        // 10 us: the bound under FIROLS_PAIR_HOLD_READY
-constexpr int kPairLead = 9;                     // default lead (measured best of 1 .. 64)
+constexpr int kPairLead = 10;                    // default lead (measured best of 1 .. 64)
 
 // XCD (XCC) the wave runs on: hardware register XCC_ID, bits 3:0.
 __device__ __forceinline__ int xcc_id() {

@@ -24,7 +24,7 @@ struct fir_ols_plan_s {
     int64_t scratch_elems = 0;    // float2 values at scratch
     int pair_nq = 0;              // split path: work queues of the paired kernel (XCD ids)
     int pair_groups = 0;          // split path: resident workgroups of the paired kernel
-    int pair_lead = 9;            // split path: producers handed out ahead of their consumers
+    int pair_lead = 10;           // split path: producers handed out ahead of their consumers
     bool pair_hold = false;       // split path: test switch FIROLS_PAIR_HOLD_READY (no flags raised)
     unsigned *err = nullptr;      // device word: 1 after a kernel wait ran out (fir_ols_check)
     // host-resident streaming (fir_ols_execute_host), created on first use
