@@ -73,6 +73,10 @@ def parse():
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="write a profiles/ summary of a rocprofv3 --kernel-trace --stats "
                          "CSV run of this script, then exit")
+    ap.add_argument("--trace-stdout", metavar="FILE", default="",
+                    help="with --summarize-trace: the traced run's standard output; its "
+                         "bench line gives each configuration's timed steps, and the "
+                         "summary adds the mean of those dispatches")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="calibrate FETCH_SIZE / WRITE_SIZE runs of this script against "
                          "the copy kernel, write profiles/ summaries, then exit")
@@ -110,6 +114,30 @@ def _file_tag(kernel: str) -> str:
     return re.sub(r"[^A-Za-z0-9]+", "_", k).strip("_")
 
 
+def _bench_line(path: str):
+    """The last JSON bench line of a run's standard output, or None."""
+    line = None
+    for ln in open(path, errors="replace"):
+        ln = ln.strip()
+        if ln.startswith("{") and '"metric"' in ln:
+            try:
+                line = json.loads(ln)
+            except ValueError:
+                pass
+    return line
+
+
+def timed_dispatches(trace_dir: str, kernel: str, n: int):
+    """Durations (us) of the last n dispatches of `kernel` (as _short prints
+    it) in a rocprofv3 kernel trace: the timed region of the bench run that
+    launched it last, since nothing launches a filtering kernel after its
+    timed steps."""
+    rows = [r for r in _csv_rows(trace_dir, "kernel_trace.csv")
+            if _short(r["Kernel_Name"]) == kernel]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    return [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows[-n:]]
+
+
 def summarize_trace(args):
     """profiles/<kernel>_<workload>_kernel_trace.md from run_kernel_stats.csv:
     one summary per configuration whose filtering kernel the run launched
@@ -119,10 +147,12 @@ def summarize_trace(args):
     rows = _csv_rows(args.summarize_trace, "kernel_stats.csv")
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     by_name = {_short(r["Name"]).split("::")[-1]: r for r in rows}
-    keys = [args.workload] if args.workload in W.PFB_WORKLOADS else list(TABLE_KEYS)
+    line = _bench_line(args.trace_stdout) if args.trace_stdout else None
+    keys = list(TABLE_KEYS) if args.workload in TABLE_KEYS else [args.workload]
     written = []
     for key in keys:
-        if key in W.PFB_WORKLOADS:
+        if key not in W.WORKLOADS:
+            # the channelizer and the multi-pass runs: the top kernel by GPU time
             r = rows[0]
         else:
             kern = roofline_kernel(W.WORKLOADS[key].N)
@@ -130,6 +160,23 @@ def summarize_trace(args):
             if r is None:
                 continue
         name = _short(r["Name"])
+        timed = []
+        if line is not None:
+            cfg = (line.get("configs") or {}).get(key)
+            if cfg is None and key == args.workload:
+                cfg = {"steps": line.get("steps"),
+                       "calls_per_step": (line.get("config") or {}).get("calls_per_step"),
+                       "avg_launch_us": (line.get("roofline") or {}).get("avg_launch_us")}
+            if cfg and cfg.get("steps") and cfg.get("calls_per_step"):
+                n = int(cfg["steps"]) * int(cfg["calls_per_step"])
+                d = timed_dispatches(args.summarize_trace, name, n)
+                if len(d) == n:
+                    timed = [f"Timed region of the traced run: its last {n} dispatches "
+                             f"({cfg['steps']} steps x {cfg['calls_per_step']} calls) average "
+                             f"{np.mean(d):.3f} us (min {min(d):.3f}, max {max(d):.3f}); the "
+                             f"bench line's avg_launch_us (HIP events around the same steps, "
+                             f"gaps between launches included) is {cfg.get('avg_launch_us')}.",
+                             ""]
         out = os.path.join(PROFILES_DIR, f"{_file_tag(name)}_{key}_kernel_trace.md")
         lines = [f"# Kernel trace: {key} ({WORKLOAD_NOTE.get(key, '')})", "",
                  "Command (working directory /tmp):", "", "```", args.command, "```", "",
@@ -139,6 +186,8 @@ def summarize_trace(args):
                  f"| `{name}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.3f} | "
                  f"{float(r['MinNs'])/1e3:.3f} | {float(r['MaxNs'])/1e3:.3f} | "
                  f"{float(r['Percentage']):.1f}% |", "",
+                 "The average covers every dispatch of the run, warm-up and parity calls "
+                 "included.", ""] + timed + [
                  "Other kernels of the same run (top 8 by GPU time):", "",
                  "| kernel | calls | average (us) | share of GPU time |", "|---|---|---|---|"]
         for o in rows[:8]:

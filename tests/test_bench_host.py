@@ -117,3 +117,38 @@ def test_trace_summary_names_the_top_kernel(tmp_path, monkeypatch):
                            "--profiles-dir", str(prof)])
     text = open(prof / "ols_fused_kernel_12_false_cfg2_kernel_trace.md").read()
     assert "| 400 | 9.000 |" in text
+
+
+def test_trace_summary_timed_region_from_the_bench_line(tmp_path, monkeypatch):
+    """With --trace-stdout the summary averages the last steps x calls
+    dispatches of the kernel, the timed region of the traced bench run."""
+    d = tmp_path / "t"
+    d.mkdir()
+    with open(d / "run_kernel_stats.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs",
+                                           "MinNs", "MaxNs", "Percentage"])
+        wr.writeheader()
+        wr.writerow({"Name": KERN, "Calls": 20, "TotalDurationNs": 2.0e5, "AverageNs": 10000,
+                     "MinNs": 8000, "MaxNs": 20000, "Percentage": 100.0})
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        wr.writeheader()
+        t = 0
+        for i in range(20):
+            # 8 slow warm-up dispatches (20 us), then 12 timed ones (8 us)
+            dur = 20000 if i < 8 else 8000
+            wr.writerow({"Kernel_Name": KERN, "Start_Timestamp": t, "End_Timestamp": t + dur})
+            t += dur + 1000
+        wr.writerow({"Kernel_Name": COPY, "Start_Timestamp": t, "End_Timestamp": t + 500})
+    out = tmp_path / "stdout.log"
+    line = {"metric": "m", "configs": {"cfg2": {"steps": 3, "calls_per_step": 4,
+                                                "avg_launch_us": 8.4}}}
+    out.write_text("some log line\n" + json.dumps(line) + "\n")
+    prof = tmp_path / "prof"
+    prof.mkdir()
+    run_main(monkeypatch, ["--workload", "cfg2", "--summarize-trace", str(d),
+                           "--trace-stdout", str(out), "--profiles-dir", str(prof)])
+    text = open(prof / "ols_fused_kernel_12_false_cfg2_kernel_trace.md").read()
+    assert "its last 12 dispatches (3 steps x 4 calls) average 8.000 us" in text
+    assert "avg_launch_us (HIP events around the same steps" in text
+    assert "is 8.4." in text
