@@ -16,8 +16,9 @@
 // counter, in groups: half 0 of `lead` consecutive blocks, then half 1 of
 // the same blocks.  Each item
 // gathers the whole block (E[q] and E[q + Ns]; the partner's second read
-// of the same lines comes from the shared L2) and runs one sub-convolution
-// on the half-resident 32768-point transform (ols_big.hpp).
+// of the same lines finds part of them in the shared L2 or the last-level
+// cache) and runs one sub-convolution on the half-resident 32768-point
+// transform (ols_big.hpp).
 //  * Half 0 (the producer) parks c_0[q] in the block's own output range at
 //    the position of R[q + Ns] (offset q + Ns - (M-1), always a kept point:
 //    all 32768 of them lie in [Ns - (M-1), L)), waits until those stores
@@ -27,11 +28,14 @@
 //    value it has just read (same thread, same address).
 // The producer took its item before the consumer took its own, so
 // it is running, and nothing it does after that waits on another
-// workgroup: the consumer's wait always ends (it is also bounded in time).
-// Producer and consumer run on the same XCD, so the parked values pass
-// through that XCD's L2 and never need to reach HBM.  A queue whose XCD
-// got no workgroup is run, after all other workgroups are done, by the
-// last workgroup to finish, both halves of each block in turn.
+// workgroup: the consumer's wait always ends.  It is also bounded in time;
+// a wait that runs out sets the plan's error word and stores NaN instead
+// of combining.  Producer and consumer run on the same XCD, so the parked
+// values pass through that XCD's L2, the point of coherence between them
+// (their non-temporal stores also write them back to memory, which the
+// output stores then overwrite).  A queue whose XCD got no workgroup is
+// run, after all other workgroups are done, by the last workgroup to
+// finish, both halves of each block in turn.
 //
 // Only blocks whose L outputs are all valid go this way (the parked values
 // need the whole output range); a call's partial last block goes through
