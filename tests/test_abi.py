@@ -76,7 +76,15 @@ def test_null_handles(lib):
     assert lib.fir_ols_set_freq_response(None, None, 8, None) == -1
     assert lib.fir_ols_set_state(None, None, None) == -1
     assert lib.fir_ols_get_state(None, None, None) == -1
+    assert lib.fir_ols_check(None, None) == -1
     assert lib.fir_ols_plan(None, 3, 8, 1) == -1
+
+
+def test_status_strings_cover_every_code(lib):
+    for code, name in fo.STATUS.items():
+        text = lib.fir_ols_status_string(code).decode()
+        assert text and text != "unknown status", name
+    assert lib.fir_ols_status_string(-9).decode().startswith("a kernel's wait")
 
 
 def test_missing_library_fails_loudly(tmp_path):

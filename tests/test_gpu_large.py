@@ -195,15 +195,18 @@ def test_large_multichannel_padded_stride_streaming(N, M):
         np.testing.assert_array_equal(st[c], oracle.state_next(x[c], s0[c], M))
 
 
-@pytest.mark.parametrize("queues", ["16", "1"])
-def test_paired_kernel_queue_counts_are_bitwise_equal(queues, monkeypatch):
-    """The N = 65536 paired kernel with its work in more queues than the
-    GPU has XCDs (the last workgroup runs the unserved ones alone) or in one
-    queue: the same outputs and state, bit for bit, as with one queue per
-    XCD; and the oracle bound on sampled outputs."""
-    say(f"paired kernel, FIROLS_PAIR_QUEUES={queues}")
+@pytest.mark.parametrize("var,value", [("FIROLS_PAIR_QUEUES", "16"), ("FIROLS_PAIR_QUEUES", "1"),
+                                       ("FIROLS_PAIR_LEAD", "1"), ("FIROLS_PAIR_LEAD", "64")])
+def test_paired_kernel_schedules_are_bitwise_equal(var, value, monkeypatch):
+    """The N = 65536 paired kernel under other schedules gives the same
+    outputs and state, bit for bit, as the default, and meets the oracle
+    bound on sampled outputs.  The schedules: its work in more queues than
+    the GPU has XCDs (the last workgroup runs the unserved ones alone), in
+    one queue, or with producers handed out 1 or 64 blocks ahead of their
+    consumers."""
+    say(f"paired kernel, {var}={value}")
     M, N = 16385, 65536
-    rng = np.random.default_rng(int(queues))
+    rng = np.random.default_rng(int(value))
     h = W.complex_taps(rng, M).astype(np.complex64)
     L = N - M + 1
     n = 37 * L + 1000
@@ -214,18 +217,18 @@ def test_paired_kernel_queue_counts_are_bitwise_equal(queues, monkeypatch):
         pa.set_freq_response(H)
         ya = run_calls(pa, x, [n], s0=s0)
         sa = pa.get_state().cpu().numpy()
-    monkeypatch.setenv("FIROLS_PAIR_QUEUES", queues)
+    monkeypatch.setenv(var, value)
     with fo.Plan(M, N, 2) as pb:
         pb.set_freq_response(H)
         yb = run_calls(pb, x, [n], s0=s0)
         sb = pb.get_state().cpu().numpy()
-    monkeypatch.delenv("FIROLS_PAIR_QUEUES")
+    monkeypatch.delenv(var)
     np.testing.assert_array_equal(yb, ya)
     np.testing.assert_array_equal(sb, sa)
     idx = np.unique(np.concatenate([np.arange(3000), W.sample_indices(5, n, 3000),
                                     np.arange(n - 2000, n)]))
     ref = oracle.fir_direct_multi(h, x, s0, idx=idx, threads=THREADS)
-    check(yb[:, idx], ref, h, x, s0, f"queues={queues}")
+    check(yb[:, idx], ref, h, x, s0, f"{var}={value}")
 
 
 def test_paired_wait_timeout_reports_error(monkeypatch):
