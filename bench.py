@@ -429,6 +429,7 @@ COMMON_DEVICE_SOURCES = ("kernel_args.hpp", "geometry.hpp", "dft.hpp", "ols_phas
                          "ols_block.hpp")
 PATH_SOURCES = {
     "fused": ("ols_fused.hip",),
+    "mid": ("ols_mid.hip", "ols_halfres.hpp"),
     "big": ("ols_big.hip", "ols_big.hpp"),
     "split": ("ols_split.hip", "ols_pair.hip", "ols_big.hpp"),
     "multi": ("ols_multi.hip", "ols_big.hpp"),
@@ -438,7 +439,8 @@ PATH_SOURCES = {
 
 def kernel_path(N: int) -> str:
     """The filtering path of a plan with N-point blocks."""
-    return ("fused" if N <= 16384 else "big" if N == 32768 else "split" if N == 65536
+    return ("fused" if N <= 8192 else "mid" if N == 16384 else "big" if N == 32768
+            else "split" if N == 65536
             else "multi")
 
 
@@ -710,7 +712,8 @@ HEADLINE = "cfg4"   # the largest configuration that fits one GPU
 def roofline_kernel(N: int) -> str:
     """Name of the filtering kernel of a plan with N-point blocks, as the
     profiles print it."""
-    return (f"ols_fused_kernel<{int(np.log2(N))}, false>" if N <= 16384 else
+    return (f"ols_fused_kernel<{int(np.log2(N))}, false>" if N <= 8192 else
+            "ols_mid_kernel<false>" if N == 16384 else
             "ols_big_kernel<false>" if N == 32768 else
             "ols_pair_kernel" if N == 65536 else "ols_multi_sub_kernel<false>")
 

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfirols.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["plan.cpp", "host_stream.cpp", "ols_fused.hip", "ols_big.hip", "ols_split.hip",
+SOURCES = ["plan.cpp", "host_stream.cpp", "ols_fused.hip", "ols_mid.hip", "ols_big.hip", "ols_split.hip",
            "ols_pair.hip", "ols_multi.hip", "pfb_plan.cpp", "pfb.hip", "static_scratch.hip"]
 ARCH = "gfx950"
 

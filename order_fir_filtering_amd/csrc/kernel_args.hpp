@@ -105,6 +105,7 @@ struct MultiArgs {
 // half-resident kernel, N = 2^kSplitLogN the split path, larger N (up to
 // kMaxLogN) the multi-pass path.
 constexpr int kFusedMaxLogN = 14;
+constexpr int kMidLogN = 14;
 constexpr int kBigLogN = 15;
 constexpr int kSplitLogN = 16;
 constexpr int kMaxLogN = 20;

@@ -42,6 +42,13 @@ int big_max_groups(int device);
 hipError_t launch_big(const FusedArgs &a, int max_groups, hipStream_t stream, bool real = false);
 hipError_t launch_big_plan_taps(const float2 *taps_padded, float2 *H, const float2 *tw,
                                 hipStream_t stream);
+// Half-resident kernel for N = 2^kMidLogN (two workgroups per CU): its
+// geometry id, resident workgroups, launches.
+int mid_geometry();
+int mid_max_groups(int device);
+hipError_t launch_mid(const FusedArgs &a, int max_groups, hipStream_t stream, bool real = false);
+hipError_t launch_mid_plan_taps(const float2 *taps_padded, float2 *H, const float2 *tw,
+                                hipStream_t stream);
 // Split path (N = 65536): radix of the split (N / 32768; 1 when
 // N <= 2^kBigLogN), twiddle tables, H order, workgroups, launches.
 int split_radix(int logn);

@@ -25,16 +25,17 @@ struct FusedCfg {
     // budget allows it (the workgroup runs many blocks, and a thread always
     // holds the same positions of each block).
     static constexpr bool REGS = G.logn <= 12;
-    // Buffer-descriptor I/O needs whole waves per block; at 1024 threads per
-    // block (128 VGPRs) its extra offsets would spill, so that size keeps
-    // pointer I/O.
+    // Buffer-descriptor I/O needs whole waves per block (N >= 1024); smaller
+    // blocks share a wave and use pointer I/O.  (N = 16384 has a kernel of
+    // its own, ols_mid.hip.)
     static constexpr bool WAVE_IO = G.TB >= 64 && G.TB < 1024;
+    static_assert(WAVE_IO || REGS, "the fused kernel covers N <= 8192");
     // At N = 8192 one block takes 66 KB of LDS and 8 waves, so two
     // workgroups fit a CU if a thread keeps to 128 VGPRs (4 waves per SIMD):
     // the second workgroup's gather and store then overlap the first one's
     // transform.  Measured with one long call at M = 2049: 94 GS/s with one
     // workgroup per CU (158 VGPRs), 131 GS/s with two (128 VGPRs, some
-    // spilled to scratch).  N = 16384 (132 KB of LDS) fits only one.
+    // spilled to scratch).
     static constexpr int MIN_WAVES_PER_SIMD = G.logn == 13 ? 4 : 1;
 };
 
@@ -192,26 +193,12 @@ __global__ __launch_bounds__(FusedCfg<GID>::WG, FusedCfg<GID>::MIN_WAVES_PER_SIM
             gather_block_wave<GID, false, true, 0, G.P, REAL>(A, gb, tb, a);
             process_block_wave<GID, REAL>(A, gb, tb, a, my, TwTable<GID>{twp, tb}, HTable<GID>{hpp, tb});
         }
-    } else if constexpr (C::REGS) {
+    } else {
         TwRegs<GID> tw;
         tw.load(A.tw, tb);
         HRegs<GID> hp;
         hp.load(A.H, tb);
         run(tw, hp);
-    } else {
-        // Table-fed: re-derive the table pointers every block (an empty asm
-        // hides that they are loop-invariant), so the compiler does not
-        // hoist the table loads out of the loop and spill them.
-        for (int64_t it = 0;; ++it) {
-            const int64_t unit = unit_of(units, blockIdx.x, gridDim.x, it);
-            if (unit < 0) break;
-            const float2 *twp = A.tw;
-            const float2 *hpp = A.H;
-            asm volatile("" : "+s"(twp), "+s"(hpp));
-            const int64_t gb = unit * C::BPW + sub;
-            filter_block<GID, REAL>(A, gb, gb < total, tb, my, TwTable<GID>{twp, tb},
-                              HTable<GID>{hpp, tb});
-        }
     }
 }
 
@@ -289,7 +276,6 @@ hipError_t launch_fused(int logn, const FusedArgs &a, int max_groups, hipStream_
         case 11: return launch_fused_t<fused_gid(11)>(a, max_groups, stream, real);
         case 12: return launch_fused_t<fused_gid(12)>(a, max_groups, stream, real);
         case 13: return launch_fused_t<fused_gid(13)>(a, max_groups, stream, real);
-        case 14: return launch_fused_t<fused_gid(14)>(a, max_groups, stream, real);
         default: return hipErrorInvalidValue;
     }
 }
@@ -327,7 +313,6 @@ int fused_max_groups(int logn, int device) {
         case 11: return max_groups_t<fused_gid(11)>(cus);
         case 12: return max_groups_t<fused_gid(12)>(cus);
         case 13: return max_groups_t<fused_gid(13)>(cus);
-        case 14: return max_groups_t<fused_gid(14)>(cus);
         default: return cus;
     }
 }
@@ -346,7 +331,6 @@ hipError_t launch_plan_taps(int logn, const float2 *taps, float2 *H, const float
         case 11: return launch_plan_t<fused_gid(11)>(taps, H, tw, stream);
         case 12: return launch_plan_t<fused_gid(12)>(taps, H, tw, stream);
         case 13: return launch_plan_t<fused_gid(13)>(taps, H, tw, stream);
-        case 14: return launch_plan_t<fused_gid(14)>(taps, H, tw, stream);
         default: return hipErrorInvalidValue;
     }
 }

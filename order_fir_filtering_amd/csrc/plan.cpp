@@ -47,11 +47,14 @@ int64_t state_len(const fir_ols_plan_s *p) { return p->nchan * (p->M - 1); }
 bool is_multi(const fir_ols_plan_s *p) { return p->logn > firols::kSplitLogN; }
 bool is_split(const fir_ols_plan_s *p) { return p->logn == firols::kSplitLogN; }
 bool is_big(const fir_ols_plan_s *p) { return p->logn == firols::kBigLogN; }
+bool is_mid(const fir_ols_plan_s *p) { return p->logn == firols::kMidLogN; }
 // split and multi-pass paths: H in the split order
 bool host_response(const fir_ols_plan_s *p) { return p->logn > firols::kBigLogN; }
 // geometry id of the plan's table builders (fused and half-resident paths)
 int table_geometry(const fir_ols_plan_s *p) {
-    return is_big(p) ? firols::big_geometry() : firols::fused_geometry(p->logn);
+    return is_big(p)   ? firols::big_geometry()
+           : is_mid(p) ? firols::mid_geometry()
+                       : firols::fused_geometry(p->logn);
 }
 
 int upload_freq_response(fir_ols_plan_t p, const float *H_host, hipStream_t s);
@@ -84,6 +87,7 @@ int fir_ols_plan(fir_ols_plan_t *out, int64_t M, int64_t N, int64_t nchan) {
     p->max_groups = multi       ? firols::multi_max_groups(p->device)
                     : split     ? firols::split_max_groups(p->device)
                     : is_big(p) ? firols::big_max_groups(p->device)
+                    : is_mid(p) ? firols::mid_max_groups(p->device)
                                 : firols::fused_max_groups(logn, p->device);
     (void)hipGetLastError();
 
@@ -164,6 +168,7 @@ int fir_ols_set_taps(fir_ols_plan_t p, const float *h_host, int64_t M, int is_co
     if (e == hipSuccess)
         e = host_response(p) ? firols::launch_split_plan_taps(p->logn, p->taps, p->H, p->tw, s)
             : is_big(p)      ? firols::launch_big_plan_taps(p->taps, p->H, p->tw, s)
+            : is_mid(p)      ? firols::launch_mid_plan_taps(p->taps, p->H, p->tw, s)
                              : firols::launch_plan_taps(p->logn, p->taps, p->H, p->tw, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return FIR_OLS_ERR_HIP;
@@ -328,8 +333,9 @@ int execute_with_scratch(fir_ols_plan_s *p, const void *x_dev, void *y_dev, int6
         a.M = (int)p->M;
         a.L = (int)p->L;
         a.nchan = (int)p->nchan;
-        e = is_big(p) ? launch_big(a, p->max_groups, s, real)
-                      : launch_fused(p->logn, a, p->max_groups, s, real);
+        e = is_big(p)   ? launch_big(a, p->max_groups, s, real)
+            : is_mid(p) ? launch_mid(a, p->max_groups, s, real)
+                        : launch_fused(p->logn, a, p->max_groups, s, real);
     }
     if (e != hipSuccess) return FIR_OLS_ERR_HIP;
     if (p->M > 1) p->parity ^= 1;
@@ -403,11 +409,12 @@ int64_t fir_ols_choose_n(int64_t M) {
     // blocks per second of N = 2^8 .. 2^20 on MI355X, measured by
     // order_fir_filtering_amd/tune_n.py (one call of many blocks per N)
     static const double kBlocksPerSecond[] = {
-        1433645823.7, 699327776.7, 375217620.0,
-        174979853.7, 71174992.1, 21326771.6,
-        7920674.7, 6919868.1, 2237289.1,
-        769852.9, 370456.1, 189607.2,
-        91014.7};
+        1413348091.7, 722691855.1, 394924269.1,
+        174677774.3, 73970396.6, 21268569.2,
+        15491336.9, 7209844.3, 2557594.1,
+        765870.6, 376224.9, 191183.2,
+        94173.3
+    };
     if (M < 1) return FIR_OLS_ERR_INVALID_ARG;
     int64_t best = FIR_OLS_ERR_UNSUPPORTED;
     double best_rate = 0.0;
