@@ -27,49 +27,8 @@ constexpr int kStaggerGroups = 3;
 constexpr uint64_t kStaggerTicks = 1000;   // 10 us of the 100 MHz constant clock
 constexpr int kStaggerMinBlocks = 3;       // blocks per workgroup for the stagger to pay
 
-// Registers R0 .. R1-1 of block gb for real-pair channels (rows 2c and
-// 2c + 1 of a float32 [2 nchan][stride] array are the real and imaginary
-// parts of channel c): two range-checked 4-byte loads per point over the
-// block's valid input, plus, for the blocks that reach into the state, one
-// 8-byte load over the (complex) state; out-of-range loads read zero.
-template <int R0, int R1>
-__device__ __forceinline__ void gather_real_big(const FusedArgs &A, int64_t gb, int tb,
-                                                float2 (&v)[kBig.P]) {
-    const int64_t c = gb / A.nblk;
-    const int64_t i = gb - c * A.nblk;
-    const int Mm1 = A.M - 1;
-    const int64_t g0 = i * A.L - Mm1;
-    const int64_t xs = g0 > 0 ? g0 : 0;
-    int64_t xn = A.nsamples - xs;
-    xn = xn < 0 ? 0 : (xn > kBig.N ? kBig.N : xn);
-    const float *x1 = (const float *)A.x + 2 * c * A.stride + xs;
-    const __amdgpu_buffer_rsrc_t r1 = buf_rsrc(x1, (uint32_t)xn * 4u);
-    const __amdgpu_buffer_rsrc_t r2 = buf_rsrc(x1 + A.stride, (uint32_t)xn * 4u);
-    const int dx = (int)(g0 - xs) + tb;          // q + dx indexes the rows from xs
-    auto ld = [](__amdgpu_buffer_rsrc_t r, uint32_t off) {
-        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-    };
-    if (g0 >= 0) {
-        static_for<R0, R1>([&](auto Rr) {
-            constexpr int r = decltype(Rr)::value;
-            const uint32_t q = (uint32_t)(kBig.TB * pass0_m<kBigGid>(r) + dx);
-            v[r] = make_float2(ld(r1, q * 4u), ld(r2, q * 4u));
-        });
-    } else {
-        const __amdgpu_buffer_rsrc_t rs = buf_rsrc(A.s0_old + c * Mm1, (uint32_t)Mm1 * 8u);
-        const int ds = (int)(g0 + Mm1) + tb;     // q + ds indexes the state
-        static_for<R0, R1>([&](auto Rr) {
-            constexpr int r = decltype(Rr)::value;
-            constexpr int q = kBig.TB * pass0_m<kBigGid>(r);
-            const uint32_t qx = (uint32_t)(q + dx);
-            const float2 st = buf_load_cached(rs, (uint32_t)(q + ds) * 8u, 0);
-            v[r] = make_float2(ld(r1, qx * 4u) + st.x, ld(r2, qx * 4u) + st.y);
-        });
-    }
-}
-
 // REAL: the channels are pairs of real float32 rows, gathered by
-// gather_real_big and stored as two float rows.
+// hr_gather_real and stored as two float rows.
 template <bool REAL>
 __global__ __launch_bounds__(kBig.TB) void ols_big_kernel(FusedArgs A) {
     __shared__ float2 lds[kHalfSlots + kTw1];
@@ -87,15 +46,15 @@ __global__ __launch_bounds__(kBig.TB) void ols_big_kernel(FusedArgs A) {
     // software-pipelined over blocks: the input of the next block is
     // requested as soon as the registers of a virtual thread are free
     int64_t gb = unit_of(units, blockIdx.x, gridDim.x, 0);
-    float2 a[kBig.P], r0[5], r1[5];
+    float2 a[kBig.P];
+    BigRows r;
     if (gb >= 0) {
         if constexpr (REAL)
-            gather_real_big<0, kBig.P>(A, gb, tb, a);
+            hr_gather_real<kBigGid, 0, kBig.P>(A, gb, tb, a);
         else
             gather_block_wave<kBigGid, true, false>(A, gb, tb, a);
         const TwBig tw0{buf_rsrc(A.tw, (uint32_t)kBig.twoff[kBig.npass] * 8u), lds_tw, tb};
-        load_pass0_rows<0>(r0, tw0);
-        load_pass0_rows<1>(r1, tw0);
+        load_big_rows(r, tw0);
     }
     for (int64_t it = 1; gb >= 0; ++it) {
         const int64_t gn = unit_of(units, blockIdx.x, gridDim.x, it);
@@ -119,7 +78,7 @@ __global__ __launch_bounds__(kBig.TB) void ols_big_kernel(FusedArgs A) {
         const __amdgpu_buffer_rsrc_t rtw = buf_rsrc(twp, (uint32_t)kBig.twoff[kBig.npass] * 8u);
         const __amdgpu_buffer_rsrc_t rh = buf_rsrc(hp, (uint32_t)kBig.N * 8u);
         big_transform(
-            tb, a, r0, r1, lds, TwBig{rtw, lds_tw, tb}, rh,
+            tb, a, r, lds, TwBig{rtw, lds_tw, tb}, rh,
             [&](auto Uu, const float2(&v)[64]) {
                 constexpr int u = decltype(Uu)::value;
                 static_for<0, 32>([&](auto J) {
@@ -137,7 +96,7 @@ __global__ __launch_bounds__(kBig.TB) void ols_big_kernel(FusedArgs A) {
                 constexpr int u = decltype(Uu)::value;
                 if (gn >= 0) {
                     if constexpr (REAL)
-                        gather_real_big<32 * u, 32 * u + 32>(A, gn, tb, v);
+                        hr_gather_real<kBigGid, 32 * u, 32 * u + 32>(A, gn, tb, v);
                     else
                         gather_block_wave<kBigGid, true, false, 32 * u, 32 * u + 32>(A, gn, tb, v);
                 }
@@ -162,30 +121,32 @@ __global__ __launch_bounds__(kBig.TB) void ols_big_plan_taps_kernel(
         a[r] = taps[tb + kBig.TB * pass0_m<kBigGid>(r)];
     });
     float2 r[5];
-    load_pass0_rows<0>(r, twt);
-    fwd_pass0_first<0>(a, r);
-    put0<0, 0>(tb, a, lds);
-    pass0_twiddles<0, 16, 32, false>(a, r);
-    load_pass0_rows<1>(r, twt);
-    fwd_pass0_first<1>(a, r);
-    put0<1, 0>(tb, a, lds);
-    pass0_twiddles<1, 16, 32, false>(a, r);
+    hr_load_rows<kBigGid, 0>(r, twt);
+    dft_at<32, -1, 0>(a);
+    hr_pass0_twiddles<kBigGid, 0, 1, 16, false>(a, r);
+    hr_put0<kBigGid, 0, 0>(tb, a, lds);
+    hr_pass0_twiddles<kBigGid, 0, 16, 32, false>(a, r);
+    hr_load_rows<kBigGid, 1>(r, twt);
+    dft_at<32, -1, 32>(a);
+    hr_pass0_twiddles<kBigGid, 1, 1, 16, false>(a, r);
+    hr_put0<kBigGid, 1, 0>(tb, a, lds);
+    hr_pass0_twiddles<kBigGid, 1, 16, 32, false>(a, r);
     constexpr float scale = 1.0f / kBig.N;
     static_for<0, 2>([&](auto Hh) {
         constexpr int h = decltype(Hh)::value;
         if constexpr (h == 1) {
             __syncthreads();
-            put0<0, 1>(tb, a, lds);
-            put0<1, 1>(tb, a, lds);
+            hr_put0<kBigGid, 0, 1>(tb, a, lds);
+            hr_put0<kBigGid, 1, 1>(tb, a, lds);
         }
         __syncthreads();
         float2 c[32];
-        get_run<33>(lds + slot1(tb), c);
-        fwd_vt<1, h>(c, twt);
-        put_run<33>(lds + slot1(tb), c);
+        hr_get_run<33>(lds + hr_slot1(tb), c);
+        hr_fwd_vt<1, h>(c, twt);
+        hr_put_run<33>(lds + hr_slot1(tb), c);
         __syncthreads();
-        get_run<1>(lds + slot2(tb), c);
-        fwd_vt<2, h>(c, twt);
+        hr_get_run<1>(lds + hr_slot2(tb), c);
+        hr_fwd_vt<2, h>(c, twt);
         static_for<0, 32>([&](auto Kk) {
             constexpr int k = decltype(Kk)::value;
             H[(32 * h + k) * kBig.TB + tb] = make_float2(c[k].x * scale, c[k].y * scale);

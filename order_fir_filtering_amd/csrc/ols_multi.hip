@@ -202,14 +202,14 @@ __global__ __launch_bounds__(kBig.TB) void ols_multi_sub_kernel(MultiArgs A, int
         });
     };
     int64_t g = unit_of(units, blockIdx.x, gridDim.x, 0);
-    float2 a[kBig.P], r0[5], r1[5];
+    float2 a[kBig.P];
+    BigRows r;
     if (g >= 0) {
         const __amdgpu_buffer_rsrc_t rs = slice(g);
         load(ic<0>{}, rs, a);
         load(ic<32>{}, rs, a);
         const TwBig tw0{buf_rsrc(A.tw, (uint32_t)kBig.twoff[kBig.npass] * 8u), lds_tw, tb};
-        load_pass0_rows<0>(r0, tw0);
-        load_pass0_rows<1>(r1, tw0);
+        load_big_rows(r, tw0);
     }
     for (int64_t it = 1; g >= 0; ++it) {
         const int64_t gn = unit_of(units, blockIdx.x, gridDim.x, it);
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kBig.TB) void ols_multi_sub_kernel(MultiArgs A, int
         const __amdgpu_buffer_rsrc_t rtw = buf_rsrc(twp, (uint32_t)kBig.twoff[kBig.npass] * 8u);
         const __amdgpu_buffer_rsrc_t rh = buf_rsrc(hp + k0 * kNs, (uint32_t)kNs * 8u);
         big_transform(
-            tb, a, r0, r1, lds, TwBig{rtw, lds_tw, tb}, rh,
+            tb, a, r, lds, TwBig{rtw, lds_tw, tb}, rh,
             [&](auto Uu, const float2(&v)[64]) {
                 constexpr int u = decltype(Uu)::value;
                 static_for<0, 32>([&](auto J) {

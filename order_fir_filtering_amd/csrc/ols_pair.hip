@@ -181,8 +181,8 @@ struct PairBlock {
 // unit's flag; wt = W_N^tb and wm the table W_N^{TB m}.
 template <bool HALF1>
 __device__ __forceinline__ void pair_item(const PairArgs &A, int64_t u, unsigned *ready, int tb,
-                                          float2 *lds, const float2 *lds_tw, float2 (&r0)[5],
-                                          float2 (&r1)[5], float2 wt, const float2 *wm) {
+                                          float2 *lds, const float2 *lds_tw, BigRows &r,
+                                          float2 wt, const float2 *wm) {
     // (the empty asm keeps the compiler from hoisting the 64 twiddle
     // products W_N^tb W_N^{TB m}, which do not depend on the item, out of
     // the item loop into spilled registers)
@@ -235,7 +235,7 @@ __device__ __forceinline__ void pair_item(const PairArgs &A, int64_t u, unsigned
     if constexpr (!HALF1) {
         // producer: each virtual thread's c_0 is parked as soon as it is
         // final, with non-temporal stores (read once, by the consumer)
-        big_transform(tb, a, r0, r1, lds, TwBig{rtw, lds_tw, tb}, rh,
+        big_transform(tb, a, r, lds, TwBig{rtw, lds_tw, tb}, rh,
                       [&](auto Uu, const float2(&v)[64]) {
                           constexpr int U = decltype(Uu)::value;
                           static_for<0, 32>([&](auto J) {
@@ -257,7 +257,7 @@ __device__ __forceinline__ void pair_item(const PairArgs &A, int64_t u, unsigned
         // whatever the output range holds.
         __shared__ int sh_ok;
         int ok = 1;
-        big_transform(tb, a, r0, r1, lds, TwBig{rtw, lds_tw, tb}, rh,
+        big_transform(tb, a, r, lds, TwBig{rtw, lds_tw, tb}, rh,
                       [&](auto Uu, const float2(&v)[64]) {
                           constexpr int U = decltype(Uu)::value;
                           if constexpr (U == 0) {
@@ -306,11 +306,10 @@ __global__ __launch_bounds__(kBig.TB) void ols_pair_kernel(PairArgs A) {
     if (tb < 64) wm[tb] = A.tw_top[kNs + kBig.TB * tb];
     const float2 wt = A.tw_top[kNs + tb];
     // (the first barrier of the item loop orders these writes before use)
-    float2 r0[5], r1[5];
+    BigRows rows;
     {
         const TwBig tw0{buf_rsrc(A.tw, (uint32_t)kBig.twoff[kBig.npass] * 8u), lds_tw, tb};
-        load_pass0_rows<0>(r0, tw0);
-        load_pass0_rows<1>(r1, tw0);
+        load_big_rows(rows, tw0);
     }
     unsigned *heads = A.sync;
     unsigned *ready = A.sync + kPairSyncHeader;
@@ -356,9 +355,9 @@ __global__ __launch_bounds__(kBig.TB) void ols_pair_kernel(PairArgs A) {
         const bool consumer = r >= nb;
         const int64_t u = lo + base + (consumer ? r - nb : r);
         if (consumer)
-            pair_item<true>(A, A.u0 + u, ready + u, tb, lds, lds_tw, r0, r1, wt, wm);
+            pair_item<true>(A, A.u0 + u, ready + u, tb, lds, lds_tw, rows, wt, wm);
         else
-            pair_item<false>(A, A.u0 + u, ready + u, tb, lds, lds_tw, r0, r1, wt, wm);
+            pair_item<false>(A, A.u0 + u, ready + u, tb, lds, lds_tw, rows, wt, wm);
     }
 }
 

@@ -156,11 +156,10 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
     const int64_t per_chan = A.nblk - A.blk0;    // blocks of each channel this launch runs
     const int64_t units = per_chan * A.nchan;
     // pass-0 twiddle rows of both virtual threads, the same for every block
-    float2 r0[5], r1[5];
+    BigRows r;
     {
         const TwBig tw0{buf_rsrc(A.tw, (uint32_t)kBig.twoff[kBig.npass] * 8u), lds_tw, tb};
-        load_pass0_rows<0>(r0, tw0);
-        load_pass0_rows<1>(r1, tw0);
+        load_big_rows(r, tw0);
     }
     for (int64_t it = 0;; ++it) {
         const int64_t gb = unit_of(units, blockIdx.x, gridDim.x, it);
@@ -236,7 +235,7 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
 
         // first half-spectrum: c_0 to the slot, a_1 back from it
         big_transform(
-            tb, a, r0, r1, lds, tw, rh0,
+            tb, a, r, lds, tw, rh0,
             [&](auto Uu, const float2(&v)[64]) {
                 constexpr int u = decltype(Uu)::value;
                 static_for<0, 32>([&](auto J) {
@@ -264,7 +263,7 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
         const __amdgpu_buffer_rsrc_t ry2 = buf_rsrc(y1 + A.stride, (uint32_t)yn * 4u);
         const int qo = tb - Mm1;
         big_transform(
-            tb, a, r0, r1, lds, tw, rh1,
+            tb, a, r, lds, tw, rh1,
             [&](auto Uu, const float2(&v)[64]) {
                 split_combine<decltype(Uu)::value, REAL>(v, tb, qo, rc0, wt, wm, ry, ry1, ry2);
             },
@@ -317,31 +316,33 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_plan_taps_kernel(
         a[r] = make_float2((float)re, (float)im);
     });
     float2 rw[5];
-    load_pass0_rows<0>(rw, twt);
-    fwd_pass0_first<0>(a, rw);
-    put0<0, 0>(tb, a, lds);
-    pass0_twiddles<0, 16, 32, false>(a, rw);
-    load_pass0_rows<1>(rw, twt);
-    fwd_pass0_first<1>(a, rw);
-    put0<1, 0>(tb, a, lds);
-    pass0_twiddles<1, 16, 32, false>(a, rw);
+    hr_load_rows<kBigGid, 0>(rw, twt);
+    dft_at<32, -1, 0>(a);
+    hr_pass0_twiddles<kBigGid, 0, 1, 16, false>(a, rw);
+    hr_put0<kBigGid, 0, 0>(tb, a, lds);
+    hr_pass0_twiddles<kBigGid, 0, 16, 32, false>(a, rw);
+    hr_load_rows<kBigGid, 1>(rw, twt);
+    dft_at<32, -1, 32>(a);
+    hr_pass0_twiddles<kBigGid, 1, 1, 16, false>(a, rw);
+    hr_put0<kBigGid, 1, 0>(tb, a, lds);
+    hr_pass0_twiddles<kBigGid, 1, 16, 32, false>(a, rw);
     const float scale = 1.0f / (float)N;   // exact: N is a power of two
     float2 *__restrict__ Hk = H + (int64_t)k0 * kNs;
     static_for<0, 2>([&](auto Hh) {
         constexpr int h = decltype(Hh)::value;
         if constexpr (h == 1) {
             __syncthreads();
-            put0<0, 1>(tb, a, lds);
-            put0<1, 1>(tb, a, lds);
+            hr_put0<kBigGid, 0, 1>(tb, a, lds);
+            hr_put0<kBigGid, 1, 1>(tb, a, lds);
         }
         __syncthreads();
         float2 c[32];
-        get_run<33>(lds + slot1(tb), c);
-        fwd_vt<1, h>(c, twt);
-        put_run<33>(lds + slot1(tb), c);
+        hr_get_run<33>(lds + hr_slot1(tb), c);
+        hr_fwd_vt<1, h>(c, twt);
+        hr_put_run<33>(lds + hr_slot1(tb), c);
         __syncthreads();
-        get_run<1>(lds + slot2(tb), c);
-        fwd_vt<2, h>(c, twt);
+        hr_get_run<1>(lds + hr_slot2(tb), c);
+        hr_fwd_vt<2, h>(c, twt);
         static_for<0, 32>([&](auto Kk) {
             constexpr int k = decltype(Kk)::value;
             Hk[(32 * h + k) * kBig.TB + tb] = make_float2(c[k].x * scale, c[k].y * scale);
