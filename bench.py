@@ -452,7 +452,8 @@ def kernel_source_hash(workload: str = "cfg2") -> str:
     import workloads as W
     w = W.WORKLOADS.get(workload)
     path = (kernel_path(w.N) if w is not None else
-            "pfb" if workload in W.PFB_WORKLOADS else "multi")
+            "pfb" if workload in W.PFB_WORKLOADS else
+            kernel_path(int(workload[1:])) if re.fullmatch(r"n\d+", workload) else "multi")
     d = os.path.join(ROOT, "order_fir_filtering_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(PATH_SOURCES[path] + COMMON_DEVICE_SOURCES):
@@ -699,6 +700,7 @@ WORKLOAD_NOTE = {
     "cfg4": "M=16385, N=65536 via H, 251658240 samples",
     "cfg5": "M=257, N=1024, 1024 channels x 65536 samples",
     "n1048576": "M=262145, N=1048576, one call of 170 blocks (tune_n.py --logn 20 20)",
+    "n16384": "M=4097, N=16384, one call of 10922 blocks (tune_n.py --logn 14 14)",
     "pfb1024": "channelizer K=1024, D=512, Nh=8192, 2^26 samples per call",
     "pfb128": "channelizer K=128, D=64, Nh=1024, 2^26 samples per call",
 }
