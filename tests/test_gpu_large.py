@@ -273,3 +273,36 @@ def test_paired_wait_timeout_reports_error(monkeypatch):
                                     np.arange(n - 2000, n)]))
     ref = oracle.fir_direct_multi(h, x, s0, idx=idx, threads=THREADS)
     check(y2[:, idx], ref, h, x, s0, "plan without the switch")
+
+
+@pytest.mark.parametrize("M,nchan,nblk", [(3000, 3, 420), (16384, 1, 1300)])
+def test_n16384_many_blocks_per_workgroup(M, nchan, nblk):
+    """N = 16384 with more blocks than resident workgroups (two per CU), so
+    each workgroup runs several blocks and requests the next block's input
+    while it finishes the current one: every output against the oracle's
+    float64 block overlap-save (H = DFT of the taps), sampled outputs
+    against the direct form, the next state bit for bit, and a second run
+    bit for bit equal to the first."""
+    N = 16384
+    L = N - M + 1
+    n = nblk * L - 123
+    say(f"N=16384 many blocks: M={M} nchan={nchan} blocks/ch={nblk} n={n}")
+    rng = np.random.default_rng(M + nblk)
+    h = W.complex_taps(rng, M).astype(np.complex64)
+    x = W.complex_normal(rng, (nchan, n))
+    s0 = W.complex_normal(rng, (nchan, M - 1))
+    with fo.Plan(M, N, nchan) as p:
+        p.set_taps(h)
+        y = run_calls(p, x, [n], s0=s0)
+        st = p.get_state().cpu().numpy()
+        y2 = run_calls(p, x, [n], s0=s0)
+    np.testing.assert_array_equal(y2, y)
+    H = np.fft.fft(np.asarray(h, dtype=np.complex128), N)
+    for c in range(nchan):
+        full = oracle.fir_ols_blocks(H, x[c], s0[c], M)
+        check(y[c], full, h, x, s0, f"N=16384 M={M} channel {c} (all {n} outputs, block OLS)")
+        np.testing.assert_array_equal(st[c], oracle.state_next(x[c], s0[c], M))
+    idx = np.unique(np.concatenate([np.arange(min(n, 2000)), W.sample_indices(M, n, 3000),
+                                    np.arange(max(0, n - 2000), n)]))
+    ref = oracle.fir_direct_multi(h, x, s0, idx=idx, threads=THREADS)
+    check(y[:, idx], ref, h, x, s0, f"N=16384 M={M} (direct form, {idx.size} outputs)")

@@ -132,15 +132,17 @@ def test_real_argument_checks():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("M,N", [(8193, 32768), (16385, 65536), (32769, 131072)])
-def test_real_rows_equal_complex_channel_bitwise_large(M, N):
+@pytest.mark.parametrize("M,N,blocks", [(4097, 16384, 700), (8193, 32768, 3), (16385, 65536, 3),
+                                        (32769, 131072, 3)])
+def test_real_rows_equal_complex_channel_bitwise_large(M, N, blocks):
     """As above for the large-N kernels: the real-pair forms compute what the
-    complex forms do on the packed channel, bit for bit."""
+    complex forms do on the packed channel, bit for bit (at N = 16384 with
+    more blocks than resident workgroups, so each runs several)."""
     import torch
     rng = np.random.default_rng(M)
     h = (rng.standard_normal(M) / np.sqrt(M)).astype(np.float32)
     HREAL[(M, N)] = h
-    n = 3 * (N - M + 1) + 777
+    n = blocks * (N - M + 1) + 777
     rows = rng.standard_normal((2, n)).astype(np.float32)
     y, _ = _run_real(M, N, rows, [n], stride_pad=0)
     z = to_dev((rows[0] + 1j * rows[1]).astype(np.complex64)[None, :])
