@@ -72,7 +72,7 @@ int pair_lead();
 bool pair_hold_ready();
 uint64_t pair_wait_ticks(bool hold);
 int pair_max_groups(int device);
-hipError_t launch_pair(const PairArgs &a, int max_groups, hipStream_t stream);
+hipError_t launch_pair(const PairArgs &a, int max_groups, hipStream_t stream, bool real = false);
 
 // Multi-pass path (N = 2^17 .. 2^20): top-pass twiddle table size and
 // builder (the sub-transform shares the split path's tables and H order),

@@ -209,7 +209,8 @@ struct ChanIn {
     const float2 *__restrict__ xc;
     const float *__restrict__ x1;
     const float *__restrict__ x2;
-    __device__ __forceinline__ ChanIn(const FusedArgs &A, int64_t c)
+    template <class ARGS>   // any call's arguments with x and stride
+    __device__ __forceinline__ ChanIn(const ARGS &A, int64_t c)
         : xc(A.x + c * A.stride),
           x1((const float *)A.x + 2 * c * A.stride),
           x2((const float *)A.x + (2 * c + 1) * A.stride) {}

@@ -39,7 +39,8 @@
 //
 // Only blocks whose L outputs are all valid go this way (the parked values
 // need the whole output range); a call's partial last block goes through
-// the one-workgroup split kernel (ols_split.hip).
+// the one-workgroup split kernel (ols_split.hip).  Real-pair channels (two
+// real rows per channel) take the same path with 4-byte row accesses.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -75,6 +76,47 @@ __device__ __forceinline__ float2 buf_load_l2(__amdgpu_buffer_rsrc_t r, uint32_t
 // Wait until every vector memory access of this wave has completed (its
 // stores written to L2): s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// The block's output range: complex channels (one descriptor over
+// [nchan][stride] complex64) or real-pair channels (rows 2c and 2c + 1 of
+// a float32 [2 nchan][stride] array, the real and imaginary parts).  Both
+// hold L values per block, so the exchange parks c_0 in the same positions
+// either way (the real-pair form splits each value over the two rows).
+// Offsets outside [0, L) (negative ones wrap to large values) are dropped
+// by the descriptors.
+template <bool REAL>
+struct PairOut;
+template <>
+struct PairOut<false> {
+    __amdgpu_buffer_rsrc_t ry;
+    __device__ __forceinline__ PairOut(const PairArgs &A, int64_t c, int64_t i)
+        : ry(buf_rsrc(A.y + c * A.stride + i * A.L, (uint32_t)A.L * 8u)) {}
+    __device__ __forceinline__ void store(float2 v, int off) const {
+        buf_store(v, ry, (uint32_t)off * 8u);
+    }
+    __device__ __forceinline__ float2 load_parked(int off) const {
+        return buf_load_l2(ry, (uint32_t)off * 8u);
+    }
+};
+template <>
+struct PairOut<true> {
+    __amdgpu_buffer_rsrc_t r1, r2;
+    __device__ __forceinline__ PairOut(const PairArgs &A, int64_t c, int64_t i) {
+        float *y1 = (float *)A.y + 2 * c * A.stride + i * A.L;
+        r1 = buf_rsrc(y1, (uint32_t)A.L * 4u);
+        r2 = buf_rsrc(y1 + A.stride, (uint32_t)A.L * 4u);
+    }
+    __device__ __forceinline__ void store(float2 v, int off) const {
+        buf_store_f32(v.x, r1, (uint32_t)off * 4u);
+        buf_store_f32(v.y, r2, (uint32_t)off * 4u);
+    }
+    __device__ __forceinline__ float2 load_parked(int off) const {
+        // sc0 + nt, as buf_load_l2
+        return make_float2(
+            __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r1, (uint32_t)off * 4u, 0, 3)),
+            __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r2, (uint32_t)off * 4u, 0, 3)));
+    }
+};
 
 // a_k of one block in the pass-0 layout (register r <-> q = tb + TB m):
 // a_0[q] = E[q] + E[q + Ns], a_1[q] = W_N^q (E[q] - E[q + Ns]), reading
@@ -121,16 +163,15 @@ __device__ __forceinline__ void pair_gather(float2 (&a)[64], const LOAD &load, f
 // c_0 - W_N^{-q} c_1 over the parked value.  kCombineAhead parked values
 // are in flight.
 constexpr int kCombineAhead = 16;
-template <int U>
+template <int U, class OUT>
 __device__ __forceinline__ void pair_combine(const float2 (&a)[64], int qo, int fo,
-                                             __amdgpu_buffer_rsrc_t ry, float2 wt,
-                                             const float2 *wm) {
+                                             const OUT &out, float2 wt, const float2 *wm) {
     constexpr int D = kCombineAhead;
     float2 c0[D];
     static_for<0, D>([&](auto Ii) {
         constexpr int i = decltype(Ii)::value;
         constexpr int off = kBig.TB * pass0_m<kBigGid>(32 * U + i);
-        c0[i] = buf_load_l2(ry, (uint32_t)(off + fo) * 8u);
+        c0[i] = out.load_parked(off + fo);
     });
     static_for<0, 32>([&](auto Ii) {
         constexpr int i = decltype(Ii)::value;
@@ -139,11 +180,11 @@ __device__ __forceinline__ void pair_combine(const float2 (&a)[64], int qo, int 
         __builtin_amdgcn_sched_barrier(0);
         const float2 b1 = cmulc(a[r], cmul(wt, wm[pass0_m<kBigGid>(r)]));
         const float2 t = c0[i % D];
-        buf_store(cadd(t, b1), ry, (uint32_t)(off + qo) * 8u);
-        buf_store(csub(t, b1), ry, (uint32_t)(off + fo) * 8u);
+        out.store(cadd(t, b1), off + qo);
+        out.store(csub(t, b1), off + fo);
         if constexpr (i + D < 32) {
             constexpr int off2 = kBig.TB * pass0_m<kBigGid>(r + D);
-            c0[(i + D) % D] = buf_load_l2(ry, (uint32_t)(off2 + fo) * 8u);
+            c0[(i + D) % D] = out.load_parked(off2 + fo);
         }
     });
     __builtin_amdgcn_sched_barrier(0);
@@ -151,13 +192,13 @@ __device__ __forceinline__ void pair_combine(const float2 (&a)[64], int qo, int 
 
 // What a consumer whose wait for c_0 timed out stores for virtual thread U
 // instead of pair_combine's values: a quiet NaN at every kept position.
-template <int U>
-__device__ __forceinline__ void pair_fill_nan(int qo, int fo, __amdgpu_buffer_rsrc_t ry) {
+template <int U, class OUT>
+__device__ __forceinline__ void pair_fill_nan(int qo, int fo, const OUT &out) {
     const float2 nan = make_float2(__builtin_nanf(""), __builtin_nanf(""));
     static_for<0, 32>([&](auto Ii) {
         constexpr int off = kBig.TB * pass0_m<kBigGid>(32 * U + decltype(Ii)::value);
-        buf_store(nan, ry, (uint32_t)(off + qo) * 8u);
-        buf_store(nan, ry, (uint32_t)(off + fo) * 8u);
+        out.store(nan, off + qo);
+        out.store(nan, off + fo);
     });
 }
 
@@ -178,8 +219,10 @@ struct PairBlock {
 };
 
 // One item: half HALF1 of unit u (block i of channel c); `ready` is the
-// unit's flag; wt = W_N^tb and wm the table W_N^{TB m}.
-template <bool HALF1>
+// unit's flag; wt = W_N^tb and wm the table W_N^{TB m}.  REAL: the
+// channels are real-pair rows (see PairOut), read with two 4-byte loads
+// per point.
+template <bool HALF1, bool REAL>
 __device__ __forceinline__ void pair_item(const PairArgs &A, int64_t u, unsigned *ready, int tb,
                                           float2 *lds, const float2 *lds_tw, BigRows &r,
                                           float2 wt, const float2 *wm) {
@@ -190,7 +233,6 @@ __device__ __forceinline__ void pair_item(const PairArgs &A, int64_t u, unsigned
     const PairBlock blk(A, u);
     const int64_t c = blk.c, i = blk.i, g0 = blk.g0;
     const int Mm1 = A.M - 1;
-    const float2 *__restrict__ xc = A.x + c * A.stride;
     const float2 *__restrict__ sc = A.s0_old + c * Mm1;
     // table pointers re-derived per item so their loads stay in the loop
     const float2 *twp = A.tw, *hp = A.H;
@@ -198,37 +240,63 @@ __device__ __forceinline__ void pair_item(const PairArgs &A, int64_t u, unsigned
     const __amdgpu_buffer_rsrc_t rtw = buf_rsrc(twp, (uint32_t)kBig.twoff[kBig.npass] * 8u);
     const __amdgpu_buffer_rsrc_t rh = buf_rsrc(hp + (HALF1 ? kNs : 0), (uint32_t)kNs * 8u);
 
+    // input sample g of the channel: complex, or the two rows' floats
+    const float2 *__restrict__ xc = A.x + c * A.stride;
+    const float *__restrict__ x1 = (const float *)A.x + 2 * c * A.stride;
+    auto ld32 = [](__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    };
     float2 a[64];
     if (g0 >= 0) {
         // a full block lies inside the input: g0 + N = (i + 1) L <= nsamples
-        const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc + g0, (uint32_t)(2 * kNs) * 8u);
-        const uint32_t vo = (uint32_t)tb * 8u;
-        pair_gather<HALF1>(a, [&](int j, int off) {
-            return buf_load_cached(rx, vo, (uint32_t)(off + j * kNs) * 8u);
-        }, wt, wm);
+        if constexpr (REAL) {
+            const __amdgpu_buffer_rsrc_t r1 = buf_rsrc(x1 + g0, (uint32_t)(2 * kNs) * 4u);
+            const __amdgpu_buffer_rsrc_t r2 =
+                buf_rsrc(x1 + A.stride + g0, (uint32_t)(2 * kNs) * 4u);
+            const uint32_t vo = (uint32_t)tb * 4u;
+            pair_gather<HALF1>(a, [&](int j, int off) {
+                const uint32_t so = (uint32_t)(off + j * kNs) * 4u;
+                return make_float2(ld32(r1, vo, so), ld32(r2, vo, so));
+            }, wt, wm);
+        } else {
+            const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc + g0, (uint32_t)(2 * kNs) * 8u);
+            const uint32_t vo = (uint32_t)tb * 8u;
+            pair_gather<HALF1>(a, [&](int j, int off) {
+                return buf_load_cached(rx, vo, (uint32_t)(off + j * kNs) * 8u);
+            }, wt, wm);
+        }
     } else {
-        // the first blocks, with the state in front: two range-checked loads
-        // per point, one over the input and one over the state; at most one
+        // the first blocks, with the state in front: range-checked loads
+        // over the input and over the (complex) state; at most one of them
         // is in range, the other reads zero
         int64_t xn = A.nsamples < 2 * kNs ? A.nsamples : 2 * kNs;
-        const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc, (uint32_t)xn * 8u);
         const __amdgpu_buffer_rsrc_t rs = buf_rsrc(sc, (uint32_t)Mm1 * 8u);
         const int dx = (int)g0 + tb;           // q + dx indexes x
         const int ds = (int)(g0 + Mm1) + tb;   // q + ds indexes the state
-        pair_gather<HALF1>(a, [&](int j, int off) {
-            const int q = off + j * kNs;
-            const float2 v = buf_load_cached(rx, (uint32_t)(q + dx) * 8u, 0);
-            const float2 s = buf_load_cached(rs, (uint32_t)(q + ds) * 8u, 0);
-            return make_float2(v.x + s.x, v.y + s.y);
-        }, wt, wm);
+        if constexpr (REAL) {
+            const __amdgpu_buffer_rsrc_t r1 = buf_rsrc(x1, (uint32_t)xn * 4u);
+            const __amdgpu_buffer_rsrc_t r2 = buf_rsrc(x1 + A.stride, (uint32_t)xn * 4u);
+            pair_gather<HALF1>(a, [&](int j, int off) {
+                const int q = off + j * kNs;
+                const float2 st = buf_load_cached(rs, (uint32_t)(q + ds) * 8u, 0);
+                return make_float2(ld32(r1, (uint32_t)(q + dx) * 4u, 0) + st.x,
+                                   ld32(r2, (uint32_t)(q + dx) * 4u, 0) + st.y);
+            }, wt, wm);
+        } else {
+            const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc, (uint32_t)xn * 8u);
+            pair_gather<HALF1>(a, [&](int j, int off) {
+                const int q = off + j * kNs;
+                const float2 v = buf_load_cached(rx, (uint32_t)(q + dx) * 8u, 0);
+                const float2 s = buf_load_cached(rs, (uint32_t)(q + ds) * 8u, 0);
+                return make_float2(v.x + s.x, v.y + s.y);
+            }, wt, wm);
+        }
     }
 
-    // the block's output range; offsets outside it (negative ones wrap to
-    // large values) are dropped by the descriptor.  The per-item bases go
-    // through an empty asm so the 64 offsets derived from them are not
-    // hoisted out of the item loop into spilled registers.
-    const __amdgpu_buffer_rsrc_t ry =
-        buf_rsrc(A.y + c * A.stride + i * A.L, (uint32_t)A.L * 8u);
+    // the block's output range.  The per-item bases go through an empty asm
+    // so the 64 offsets derived from them are not hoisted out of the item
+    // loop into spilled registers.
+    const PairOut<REAL> out(A, c, i);
     int qo = tb - Mm1;
     int fo = tb + kNs - Mm1;
     asm volatile("" : "+v"(qo), "+v"(fo));
@@ -241,7 +309,7 @@ __device__ __forceinline__ void pair_item(const PairArgs &A, int64_t u, unsigned
                           static_for<0, 32>([&](auto J) {
                               constexpr int r = 32 * U + decltype(J)::value;
                               constexpr int off = kBig.TB * pass0_m<kBigGid>(r);
-                              buf_store(v[r], ry, (uint32_t)(off + fo) * 8u);
+                              out.store(v[r], off + fo);
                           });
                       },
                       [](auto, float2(&)[64]) {});
@@ -283,18 +351,20 @@ __device__ __forceinline__ void pair_item(const PairArgs &A, int64_t u, unsigned
                               ok = __builtin_amdgcn_readfirstlane(sh_ok);
                           }
                           if (ok)
-                              pair_combine<U>(v, qo, fo, ry, wt, wm);
+                              pair_combine<U>(v, qo, fo, out, wt, wm);
                           else
-                              pair_fill_nan<U>(qo, fo, ry);
+                              pair_fill_nan<U>(qo, fo, out);
                       },
                       [](auto, float2(&)[64]) {});
         if (i == A.nblk - 1)
-            carry_state<kBigGid>(A.nsamples, Mm1, tb, xc, sc, A.s0_new + c * Mm1);
+            carry_state<kBigGid>(A.nsamples, Mm1, tb, ChanIn<REAL>(A, c), sc,
+                                 A.s0_new + c * Mm1);
     }
 }
 
 }  // namespace
 
+template <bool REAL>
 __global__ __launch_bounds__(kBig.TB) void ols_pair_kernel(PairArgs A) {
     __shared__ float2 lds[kHalfSlots + kTw1];
     __shared__ int sh_word;
@@ -355,9 +425,9 @@ __global__ __launch_bounds__(kBig.TB) void ols_pair_kernel(PairArgs A) {
         const bool consumer = r >= nb;
         const int64_t u = lo + base + (consumer ? r - nb : r);
         if (consumer)
-            pair_item<true>(A, A.u0 + u, ready + u, tb, lds, lds_tw, rows, wt, wm);
+            pair_item<true, REAL>(A, A.u0 + u, ready + u, tb, lds, lds_tw, rows, wt, wm);
         else
-            pair_item<false>(A, A.u0 + u, ready + u, tb, lds, lds_tw, rows, wt, wm);
+            pair_item<false, REAL>(A, A.u0 + u, ready + u, tb, lds, lds_tw, rows, wt, wm);
     }
 }
 
@@ -432,14 +502,20 @@ int pair_max_groups(int device) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
         cus < 1)
         cus = 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ols_pair_kernel, kBig.TB, 0) !=
-            hipSuccess ||
+    // the plan's workgroup count serves both variants: the smaller occupancy
+    int per_cu_real = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ols_pair_kernel<false>, kBig.TB,
+                                                     0) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_real, ols_pair_kernel<true>,
+                                                     kBig.TB, 0) == hipSuccess &&
+        per_cu_real >= 1 && per_cu_real < per_cu)
+        per_cu = per_cu_real;
     return cus * per_cu;
 }
 
-hipError_t launch_pair(const PairArgs &call, int max_groups, hipStream_t stream) {
+hipError_t launch_pair(const PairArgs &call, int max_groups, hipStream_t stream, bool real) {
     const int64_t units = call.nfull * call.nchan;
     if (units <= 0 || call.nq < 1 || call.nq > kPairMaxQueues || max_groups < 1)
         return hipErrorInvalidConfiguration;
@@ -453,7 +529,12 @@ hipError_t launch_pair(const PairArgs &call, int max_groups, hipStream_t stream)
                            a.sync, words);
         int64_t grid = 2 * (int64_t)a.nu;
         if (grid > max_groups) grid = max_groups;
-        hipLaunchKernelGGL(ols_pair_kernel, dim3((unsigned)grid), dim3(kBig.TB), 0, stream, a);
+        if (real)
+            hipLaunchKernelGGL(ols_pair_kernel<true>, dim3((unsigned)grid), dim3(kBig.TB), 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL(ols_pair_kernel<false>, dim3((unsigned)grid), dim3(kBig.TB), 0,
+                               stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -269,10 +269,9 @@ int execute_with_scratch(fir_ols_plan_s *p, const void *x_dev, void *y_dev, int6
         const int64_t slot = split_slot_elems(p->logn);
         const int64_t slots = scratch_elems / slot - 1;
         if (!scratch || slots < 1) return FIR_OLS_ERR_UNSUPPORTED;
-        // blocks whose L outputs are all valid go to the paired kernel
-        // (complex input); a partial last block, and real-pair input, to the
-        // one-workgroup kernel
-        const int64_t nfull = real ? 0 : nsamples / p->L;
+        // blocks whose L outputs are all valid go to the paired kernel; a
+        // partial last block to the one-workgroup kernel
+        const int64_t nfull = nsamples / p->L;
         if (nfull > 0) {
             PairArgs a;
             a.x = (const float2 *)x_dev;
@@ -297,7 +296,7 @@ int execute_with_scratch(fir_ols_plan_s *p, const void *x_dev, void *y_dev, int6
             a.M = (int)p->M;
             a.L = (int)p->L;
             a.nchan = (int)p->nchan;
-            e = launch_pair(a, p->pair_groups, s);
+            e = launch_pair(a, p->pair_groups, s, real);
         }
         if (e == hipSuccess && nfull < nblk) {
             const int groups = (int)(slots < p->max_groups ? slots : p->max_groups);
