@@ -717,7 +717,7 @@ def roofline_kernel(N: int) -> str:
     return (f"ols_fused_kernel<{int(np.log2(N))}, false>" if N <= 8192 else
             "ols_mid_kernel<false>" if N == 16384 else
             "ols_big_kernel<false>" if N == 32768 else
-            "ols_pair_kernel" if N == 65536 else "ols_multi_sub_kernel<false>")
+            "ols_pair_kernel<false>" if N == 65536 else "ols_multi_sub_kernel<false>")
 
 
 def measure(key, fo, torch, *, steps, warmup, timed_ms, warm_ms, cpu_budget, cpu_single_s,
