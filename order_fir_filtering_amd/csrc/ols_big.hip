@@ -81,14 +81,15 @@ __global__ __launch_bounds__(kBig.TB) void ols_big_kernel(FusedArgs A) {
             tb, a, r, lds, TwBig{rtw, lds_tw, tb}, rh,
             [&](auto Uu, const float2(&v)[64]) {
                 constexpr int u = decltype(Uu)::value;
+                const int qu = fresh_v(qo);
                 static_for<0, 32>([&](auto J) {
                     constexpr int r = 32 * u + decltype(J)::value;
-                    const uint32_t q = (uint32_t)(qo + kBig.TB * pass0_m<kBigGid>(r));
+                    const int q = qu + kBig.TB * pass0_m<kBigGid>(r);
                     if constexpr (REAL) {
-                        buf_store_f32(v[r].x, ry1, q * 4u);
-                        buf_store_f32(v[r].y, ry2, q * 4u);
+                        buf_store_f32(v[r].x, ry1, buf_off<4>(q));
+                        buf_store_f32(v[r].y, ry2, buf_off<4>(q));
                     } else {
-                        buf_store(v[r], ry, q * 8u);
+                        buf_store(v[r], ry, buf_off<8>(q));
                     }
                 });
             },

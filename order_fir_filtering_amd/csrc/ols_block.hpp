@@ -161,6 +161,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uin
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                              0x00020000);
 }
+// Byte offset of element e (SIZE bytes per element) for a range-checked
+// buffer access where e may be negative: a position before the buffer,
+// to read as zero or to drop.  A negative e wraps to 2^32 - SIZE |e|,
+// which is at least 2^31 here (|e| stays below 2^21); every byte offset at
+// or above 2^30 becomes 2^30, past every buffer these accesses use (at
+// most 2^20 elements of 8 bytes).  The plain wrap is not safe: a 4-byte
+// access whose lanes held wrapped offsets just below 2^32 next to in-range
+// lanes at 0, 4, ... read zero for those in-range lanes too (and such
+// stores were dropped), when M - 1 was not a multiple of 4.  With e a
+// per-thread base plus a constant this is one v_add and one v_min.
+template <int SIZE>
+__device__ __forceinline__ uint32_t buf_off(int e) {
+    const uint32_t b = (uint32_t)e * (uint32_t)SIZE;
+    return b < 0x40000000u ? b : 0x40000000u;
+}
+
+// v through an empty asm: the offsets derived from it are formed where
+// they are used instead of being hoisted out of the block loop and kept
+// live (64 clamped offsets per thread would spill)
+__device__ __forceinline__ int fresh_v(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 // Non-temporal load (cache-policy bit 1): for input that the small-block
 // kernel streams through once when every workgroup has a single block
 // (several blocks per workgroup measured faster with the default policy,
@@ -320,7 +344,7 @@ __device__ __forceinline__ void gather_block_wave(const FusedArgs &A, int64_t gb
         const int ds = (int)(g0 + Mm1) + tb;    // q + ds indexes the state
         static_for<R0, R1>([&](auto Rr) {
             constexpr int off = G.TB * pass0_m<GID>(decltype(Rr)::value);
-            const float2 u = buf_load_policy<NT>(rx, (uint32_t)(off + dx) * 8u, 0);
+            const float2 u = buf_load_policy<NT>(rx, buf_off<8>(off + dx), 0);
             const float2 v = buf_load_policy<NT>(rs, (uint32_t)(off + ds) * 8u, 0);
             a[decltype(Rr)::value] = make_float2(u.x + v.x, u.y + v.y);
         });
@@ -366,8 +390,8 @@ __device__ __forceinline__ void store_block_wave(const FusedArgs &A, int64_t gb,
         static_for<0, G.P>([&](auto Rr) {
             constexpr int r = decltype(Rr)::value;
             const int q = tb + G.TB * pass0_m<GID>(r);
-            buf_store_f32(a[r].x, r1, (uint32_t)(q - Mm1) * 4u);
-            buf_store_f32(a[r].y, r2, (uint32_t)(q - Mm1) * 4u);
+            buf_store_f32(a[r].x, r1, buf_off<4>(q - Mm1));
+            buf_store_f32(a[r].y, r2, buf_off<4>(q - Mm1));
         });
     } else {
         const __amdgpu_buffer_rsrc_t ry =
@@ -375,7 +399,7 @@ __device__ __forceinline__ void store_block_wave(const FusedArgs &A, int64_t gb,
         static_for<0, G.P>([&](auto Rr) {
             constexpr int r = decltype(Rr)::value;
             const int q = tb + G.TB * pass0_m<GID>(r);
-            buf_store(a[r], ry, (uint32_t)(q - Mm1) * 8u);
+            buf_store(a[r], ry, buf_off<8>(q - Mm1));
         });
     }
 

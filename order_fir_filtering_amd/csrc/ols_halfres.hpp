@@ -247,9 +247,9 @@ __device__ __forceinline__ void hr_gather_real(const FusedArgs &A, int64_t gb, i
         static_for<R0, R1>([&](auto Rr) {
             constexpr int r = decltype(Rr)::value;
             constexpr int q = G.TB * pass0_m<GID>(r);
-            const uint32_t qx = (uint32_t)(q + dx);
+            const uint32_t qx = buf_off<4>(q + dx);
             const float2 st = buf_load_cached(rs, (uint32_t)(q + ds) * 8u, 0);
-            v[r] = make_float2(ld(r1, qx * 4u) + st.x, ld(r2, qx * 4u) + st.y);
+            v[r] = make_float2(ld(r1, qx) + st.x, ld(r2, qx) + st.y);
         });
     }
 }

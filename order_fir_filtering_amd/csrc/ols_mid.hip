@@ -74,14 +74,15 @@ __global__ __launch_bounds__(Mid::TB, 2) void ols_mid_kernel(FusedArgs A) {
             tb, a, r, lds, TwHalfRes<kMidGid>{rtw, lds_tw, tb}, rh,
             [&](auto Uu, const float2(&v)[64]) {
                 constexpr int u = decltype(Uu)::value;
+                const int qu = fresh_v(qo);
                 static_for<0, Mid::R0>([&](auto J) {
                     constexpr int rr = Mid::R0 * u + decltype(J)::value;
-                    const uint32_t q = (uint32_t)(qo + G.TB * pass0_m<kMidGid>(rr));
+                    const int q = qu + G.TB * pass0_m<kMidGid>(rr);
                     if constexpr (REAL) {
-                        buf_store_f32(v[rr].x, ry1, q * 4u);
-                        buf_store_f32(v[rr].y, ry2, q * 4u);
+                        buf_store_f32(v[rr].x, ry1, buf_off<4>(q));
+                        buf_store_f32(v[rr].y, ry2, buf_off<4>(q));
                     } else {
-                        buf_store(v[rr], ry, q * 8u);
+                        buf_store(v[rr], ry, buf_off<8>(q));
                     }
                 });
             },

@@ -82,8 +82,8 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // a float32 [2 nchan][stride] array, the real and imaginary parts).  Both
 // hold L values per block, so the exchange parks c_0 in the same positions
 // either way (the real-pair form splits each value over the two rows).
-// Offsets outside [0, L) (negative ones wrap to large values) are dropped
-// by the descriptors.
+// Offsets outside [0, L) are dropped by the descriptors (negative ones
+// through buf_off, which keeps them clear of the in-range offsets).
 template <bool REAL>
 struct PairOut;
 template <>
@@ -92,10 +92,10 @@ struct PairOut<false> {
     __device__ __forceinline__ PairOut(const PairArgs &A, int64_t c, int64_t i)
         : ry(buf_rsrc(A.y + c * A.stride + i * A.L, (uint32_t)A.L * 8u)) {}
     __device__ __forceinline__ void store(float2 v, int off) const {
-        buf_store(v, ry, (uint32_t)off * 8u);
+        buf_store(v, ry, buf_off<8>(off));
     }
     __device__ __forceinline__ float2 load_parked(int off) const {
-        return buf_load_l2(ry, (uint32_t)off * 8u);
+        return buf_load_l2(ry, buf_off<8>(off));
     }
 };
 template <>
@@ -107,14 +107,14 @@ struct PairOut<true> {
         r2 = buf_rsrc(y1 + A.stride, (uint32_t)A.L * 4u);
     }
     __device__ __forceinline__ void store(float2 v, int off) const {
-        buf_store_f32(v.x, r1, (uint32_t)off * 4u);
-        buf_store_f32(v.y, r2, (uint32_t)off * 4u);
+        buf_store_f32(v.x, r1, buf_off<4>(off));
+        buf_store_f32(v.y, r2, buf_off<4>(off));
     }
     __device__ __forceinline__ float2 load_parked(int off) const {
         // sc0 + nt, as buf_load_l2
         return make_float2(
-            __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r1, (uint32_t)off * 4u, 0, 3)),
-            __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r2, (uint32_t)off * 4u, 0, 3)));
+            __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r1, buf_off<4>(off), 0, 3)),
+            __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r2, buf_off<4>(off), 0, 3)));
     }
 };
 
@@ -279,14 +279,14 @@ __device__ __forceinline__ void pair_item(const PairArgs &A, int64_t u, unsigned
             pair_gather<HALF1>(a, [&](int j, int off) {
                 const int q = off + j * kNs;
                 const float2 st = buf_load_cached(rs, (uint32_t)(q + ds) * 8u, 0);
-                return make_float2(ld32(r1, (uint32_t)(q + dx) * 4u, 0) + st.x,
-                                   ld32(r2, (uint32_t)(q + dx) * 4u, 0) + st.y);
+                return make_float2(ld32(r1, buf_off<4>(q + dx), 0) + st.x,
+                                   ld32(r2, buf_off<4>(q + dx), 0) + st.y);
             }, wt, wm);
         } else {
             const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc, (uint32_t)xn * 8u);
             pair_gather<HALF1>(a, [&](int j, int off) {
                 const int q = off + j * kNs;
-                const float2 v = buf_load_cached(rx, (uint32_t)(q + dx) * 8u, 0);
+                const float2 v = buf_load_cached(rx, buf_off<8>(q + dx), 0);
                 const float2 s = buf_load_cached(rs, (uint32_t)(q + ds) * 8u, 0);
                 return make_float2(v.x + s.x, v.y + s.y);
             }, wt, wm);

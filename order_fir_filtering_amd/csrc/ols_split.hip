@@ -104,13 +104,13 @@ __device__ __forceinline__ void split_combine(const float2 (&v)[64], int tb, int
             const float2 b1 = cmulc(v[r], cmul(wt, wm[pass0_m<kBigGid>(r)]));
             const float2 y0 = cadd(c0[g & 1][i], b1), y1 = csub(c0[g & 1][i], b1);
             if constexpr (REAL) {
-                buf_store_f32(y0.x, ry1, (uint32_t)(qo + off) * 4u);
-                buf_store_f32(y0.y, ry2, (uint32_t)(qo + off) * 4u);
-                buf_store_f32(y1.x, ry1, (uint32_t)(qo + off + kNs) * 4u);
-                buf_store_f32(y1.y, ry2, (uint32_t)(qo + off + kNs) * 4u);
+                buf_store_f32(y0.x, ry1, buf_off<4>(qo + off));
+                buf_store_f32(y0.y, ry2, buf_off<4>(qo + off));
+                buf_store_f32(y1.x, ry1, buf_off<4>(qo + off + kNs));
+                buf_store_f32(y1.y, ry2, buf_off<4>(qo + off + kNs));
             } else {
-                buf_store(y0, ry, (uint32_t)(qo + off) * 8u);
-                buf_store(y1, ry, (uint32_t)(qo + off + kNs) * 8u);
+                buf_store(y0, ry, buf_off<8>(qo + off));
+                buf_store(y1, ry, buf_off<8>(qo + off + kNs));
             }
         });
     });
@@ -211,8 +211,8 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
             split_gather(a, tb, [&](int j, int off) {
                 const int q = off + j * kNs;
                 const float2 v = buf_load_cached(rs, (uint32_t)(q + ds) * 8u, 0);
-                return make_float2(buf_load_f32_cached(rx1, (uint32_t)(q + dx) * 4u, 0) + v.x,
-                                   buf_load_f32_cached(rx2, (uint32_t)(q + dx) * 4u, 0) + v.y);
+                return make_float2(buf_load_f32_cached(rx1, buf_off<4>(q + dx), 0) + v.x,
+                                   buf_load_f32_cached(rx2, buf_off<4>(q + dx), 0) + v.y);
             }, wt, wm, ra1);
         } else {
             // first blocks (state in front) and the partial last block: two
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
             const int ds = (int)(g0 + Mm1) + tb;    // q + ds indexes the state
             split_gather(a, tb, [&](int j, int off) {
                 const int q = off + j * kNs;
-                const float2 u = buf_load_cached(rx, (uint32_t)(q + dx) * 8u, 0);
+                const float2 u = buf_load_cached(rx, buf_off<8>(q + dx), 0);
                 const float2 v = buf_load_cached(rs, (uint32_t)(q + ds) * 8u, 0);
                 return make_float2(u.x + v.x, u.y + v.y);
             }, wt, wm, ra1);
@@ -265,7 +265,8 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
         big_transform(
             tb, a, r, lds, tw, rh1,
             [&](auto Uu, const float2(&v)[64]) {
-                split_combine<decltype(Uu)::value, REAL>(v, tb, qo, rc0, wt, wm, ry, ry1, ry2);
+                split_combine<decltype(Uu)::value, REAL>(v, tb, fresh_v(qo), rc0, wt, wm, ry, ry1,
+                                                         ry2);
             },
             [&](auto, float2(&)[64]) {});
 

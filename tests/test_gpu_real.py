@@ -153,3 +153,53 @@ def test_real_rows_equal_complex_channel_bitwise_large(M, N, blocks):
     yz = yz.cpu().numpy()[0]
     np.testing.assert_array_equal(y[0], yz.real)
     np.testing.assert_array_equal(y[1], yz.imag)
+
+
+@pytest.mark.parametrize("N,Mm1", [(16384, 1769), (16384, 1770), (16384, 1771),
+                                   (32768, 2997), (32768, 2998), (32768, 2999),
+                                   (65536, 9001), (65536, 9002), (65536, 9003)])
+def test_real_rows_with_state_length_not_a_multiple_of_four(N, Mm1):
+    """Every output near the start of each call, at M - 1 = 1, 2, 3 (mod 4)
+    and N = 16384, 32768, 65536.  In the first block of a call, the threads
+    below M - 1 index the input at negative positions (the state lies
+    there) while their neighbours read x[0], x[1], ...; with 4-byte rows
+    the neighbours' offsets 0, 4, 8 sit next to wrapped negative ones, and
+    the outputs that hold x[0] .. x[2] (and, in the paired kernel, the
+    stores of outputs 0 and 1) must still be right.  The complex channel of
+    the same rows must agree bit for bit."""
+    import torch
+    M = Mm1 + 1
+    say(f"real rows, M-1 mod 4 = {Mm1 % 4}: M={M} N={N}")
+    rng = np.random.default_rng(Mm1)
+    h = (rng.standard_normal(M) / np.sqrt(M)).astype(np.float32)
+    HREAL[(M, N)] = h
+    L = N - Mm1
+    calls = [2 * L + 501, 3 * L + 77]
+    n = sum(calls)
+    rows = rng.standard_normal((2, n)).astype(np.float32)
+    s1 = rng.standard_normal((2, Mm1)).astype(np.float32)
+    s0c = (s1[0::2] + 1j * s1[1::2]).astype(np.complex64)
+    y, st = _run_real(M, N, rows, calls, s0c)
+    starts = np.concatenate([np.arange(0, M + 256), calls[0] + np.arange(0, M + 256)])
+    idx = np.unique(np.concatenate([starts, np.arange(0, n, 13), [n - 1]]))
+    for r in range(2):
+        xr = rows[r:r + 1].astype(np.complex64)
+        sr = s1[r:r + 1].astype(np.complex64)
+        ref = oracle.fir_direct_multi(h, xr, sr, idx=idx, threads=THREADS)
+        check(y[r:r + 1, idx], ref.real, h, xr, sr, f"row {r}")
+    want = oracle.state_next(rows[0] + 1j * rows[1], s0c[0], M)
+    np.testing.assert_array_equal(st[0], want.astype(np.complex64))
+    # the packed complex channel, same calls, same state
+    z = to_dev((rows[0] + 1j * rows[1]).astype(np.complex64)[None, :])
+    yz = torch.empty_like(z)
+    with fo.Plan(M, N, 1) as p:
+        p.set_taps(h)
+        p.set_state(to_dev(s0c))
+        pos = 0
+        for c in calls:
+            yz[:, pos:pos + c] = p.execute(z[:, pos:pos + c].contiguous())
+            pos += c
+        torch.cuda.synchronize()
+    yz = yz.cpu().numpy()[0]
+    np.testing.assert_array_equal(y[0], yz.real)
+    np.testing.assert_array_equal(y[1], yz.imag)
