@@ -50,7 +50,7 @@ enum {
     FIR_OLS_ERR_UNSUPPORTED = -2,  /* size outside what the kernels cover */
     FIR_OLS_ERR_NO_FILTER = -3,    /* execute before set_taps/set_freq_response */
     FIR_OLS_ERR_ALIAS = -4,        /* input and output memory overlap */
-    FIR_OLS_ERR_ALIGN = -5,        /* device pointer not 8-byte aligned */
+    FIR_OLS_ERR_ALIGN = -5,        /* device pointer not aligned to its element (8 bytes; 4 for real rows) */
     FIR_OLS_ERR_OOM = -6,          /* device allocation failed */
     FIR_OLS_ERR_HIP = -7,          /* HIP runtime error (launch, copy, sync) */
     FIR_OLS_ERR_DEVICE = -8,       /* current device is not the plan's device */

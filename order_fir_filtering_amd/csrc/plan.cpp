@@ -440,7 +440,7 @@ const char *fir_ols_status_string(int status) {
         case FIR_OLS_ERR_UNSUPPORTED: return "unsupported size";
         case FIR_OLS_ERR_NO_FILTER: return "no filter set";
         case FIR_OLS_ERR_ALIAS: return "input and output overlap";
-        case FIR_OLS_ERR_ALIGN: return "pointer not 8-byte aligned";
+        case FIR_OLS_ERR_ALIGN: return "pointer not aligned to its element size";
         case FIR_OLS_ERR_OOM: return "device allocation failed";
         case FIR_OLS_ERR_HIP: return "HIP runtime error";
         case FIR_OLS_ERR_DEVICE: return "current device is not the plan's device";
