@@ -1,4 +1,5 @@
-"""Seeded random sweep over every kernel family, every output checked.
+"""Seeded random sweeps over every kernel family and entry point, every
+output checked.
 
 Each case draws N (8 .. 2^20, so the fused, 16384, 32768, paired/split and
 multi-pass kernels all appear), M (1, 2, small, up to N/2, up to N, and a
@@ -103,4 +104,71 @@ def test_random_case_matches_block_ols(k):
     for c in range(nchan):
         ref = oracle.fir_ols_blocks(H, x[c], s0[c], M)
         check(got[c], ref, h, x[c:c + 1], s0[c:c + 1], f"case {k} ch {c}")
+        np.testing.assert_array_equal(st[c], oracle.state_next(x[c], s0[c], M))
+
+
+NMIXED = 16
+
+
+@pytest.mark.parametrize("k", range(NMIXED))
+def test_random_mixed_entry_points_carry_one_stream(k):
+    """Consecutive calls on one plan through fir_ols_execute,
+    fir_ols_execute_static (no allocation) and fir_ols_execute_host
+    (host-resident, random chunk sizes) in random order: together they must
+    filter the stream as one pass does, every output and the final state."""
+    import torch
+    rng = np.random.default_rng(30_000 + k)
+    N = 1 << int(rng.choice([5, 8, 10, 12, 14, 15, 16, 17]))
+    M = int(rng.choice([1, int(rng.integers(2, N // 2 + 1)), int(rng.integers(N // 2, N + 1))]))
+    L = N - M + 1
+    nchan = int(rng.integers(1, 4))
+    n = max(1, min(int(rng.integers(1, 7)) * L + int(rng.integers(-L + 1, L)), 600_000 // nchan))
+    ncalls = int(rng.integers(2, 7))
+    cuts = (sorted(rng.choice(np.arange(1, n), size=min(ncalls - 1, n - 1), replace=False))
+            if n > 1 else [])
+    calls = [int(c) for c in np.diff([0] + [int(c) for c in cuts] + [n])]
+    kinds = [str(rng.choice(["dev", "static", "host"])) for _ in calls]
+    pad = int(rng.choice([0, 5]))
+    say(f"mixed case {k}: N={N} M={M} nchan={nchan} n={n} calls={calls} kinds={kinds}")
+    stride = n + pad
+    h = W.complex_taps(rng, M).astype(np.complex64)
+    x = W.complex_normal(rng, (nchan, n))
+    s0 = W.complex_normal(rng, (nchan, M - 1))
+    xp = np.zeros((nchan, stride), np.complex64)
+    xp[:, :n] = x
+    xd = to_dev(xp)
+    yd = torch.full_like(xd, 7.0)
+    xh = torch.from_numpy(xp).pin_memory()
+    yh = torch.full_like(xh, 7.0).pin_memory()
+    on_host = np.zeros(n, bool)
+    with fo.Plan(M, N, nchan) as p:
+        p.set_taps(h)
+        p.set_state(to_dev(s0))
+        pos = 0
+        for c, kd in zip(calls, kinds):
+            off = 8 * pos
+            if kd == "dev":
+                fo.fir_ols_execute(p.handle, xd.data_ptr() + off, yd.data_ptr() + off, c, stride)
+            elif kd == "static":
+                fo.fir_ols_execute_static(p.handle, xd.data_ptr() + off, yd.data_ptr() + off, c,
+                                          stride)
+            else:
+                # (one-sample chunks, one launch per sample, on short calls only)
+                chunk = int(rng.choice([0, 1 if c <= 200 else L, L, 3 * L + 5]))
+                fo.fir_ols_execute_host(p.handle, xh.data_ptr() + off, yh.data_ptr() + off, c,
+                                        stride, chunk)
+                on_host[pos:pos + c] = True
+            pos += c
+        st = p.get_state().cpu().numpy()
+        torch.cuda.synchronize()
+        p.check()
+    y = yd.cpu().numpy().copy()
+    yhost = yh.numpy()
+    assert np.all(y[:, n:] == 7.0) and np.all(yhost[:, n:] == 7.0)
+    y = y[:, :n]
+    y[:, on_host] = yhost[:, :n][:, on_host]
+    H = np.fft.fft(np.asarray(h, np.complex128), N)
+    for c in range(nchan):
+        ref = oracle.fir_ols_blocks(H, x[c], s0[c], M)
+        check(y[c], ref, h, x[c:c + 1], s0[c:c + 1], f"mixed case {k} ch {c}")
         np.testing.assert_array_equal(st[c], oracle.state_next(x[c], s0[c], M))
