@@ -306,3 +306,39 @@ def test_n16384_many_blocks_per_workgroup(M, nchan, nblk):
                                     np.arange(max(0, n - 2000), n)]))
     ref = oracle.fir_direct_multi(h, x, s0, idx=idx, threads=THREADS)
     check(y[:, idx], ref, h, x, s0, f"N=16384 M={M} (direct form, {idx.size} outputs)")
+
+
+@pytest.mark.parametrize("M,nchan,nfull", [(65536, 1, 70000), (65000, 2, 33000)])
+def test_paired_kernel_more_units_than_one_launch(M, nchan, nfull):
+    """More full blocks than one paired launch takes (65536 channel-blocks):
+    the call runs as several launches, the later ones starting at a unit
+    offset with their own cleared counters and flags.  M = N gives a block
+    length of 1, so 70000 samples are 70000 full blocks (every output
+    checked, and only the last position of each block is kept); M = 65000
+    over two channels puts the launch boundary inside the second channel
+    (blocks around it checked in full) and leaves a partial last block."""
+    N = 65536
+    L = N - M + 1
+    n = nfull * L + L // 2
+    say(f"paired launches: M={M} nchan={nchan} full blocks={nfull} n={n}")
+    rng = np.random.default_rng(M + nchan)
+    h = W.complex_taps(rng, M).astype(np.complex64)
+    x = W.complex_normal(rng, (nchan, n))
+    s0 = W.complex_normal(rng, (nchan, M - 1))
+    with fo.Plan(M, N, nchan) as p:
+        p.set_taps(h)
+        y = run_calls(p, x, [n], s0=s0)
+        st = p.get_state().cpu().numpy()
+        p.check()
+    if n <= 100_000:
+        idx = np.arange(n)
+    else:
+        c_b, i_b = divmod(65536, nfull)               # first unit of the second launch
+        assert c_b < nchan
+        near = [np.arange(b * L, (b + 1) * L) for b in (i_b - 1, i_b, i_b + 1)]
+        idx = np.unique(np.concatenate(near + [np.arange(2000), np.arange(n - 2000, n),
+                                               W.sample_indices(M, n, 3000)]))
+    ref = oracle.fir_direct_multi(h, x, s0, idx=idx, threads=THREADS)
+    check(y[:, idx], ref, h, x, s0, f"M={M} nchan={nchan} nfull={nfull}")
+    for c in range(nchan):
+        np.testing.assert_array_equal(st[c], oracle.state_next(x[c], s0[c], M))
