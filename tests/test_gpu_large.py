@@ -342,3 +342,43 @@ def test_paired_kernel_more_units_than_one_launch(M, nchan, nfull):
     check(y[:, idx], ref, h, x, s0, f"M={M} nchan={nchan} nfull={nfull}")
     for c in range(nchan):
         np.testing.assert_array_equal(st[c], oracle.state_next(x[c], s0[c], M))
+
+
+def test_partial_last_blocks_outnumber_the_slots():
+    """N = 65536 with 300 channels of one full and one partial block: the
+    300 partial blocks go to the one-workgroup kernel, which holds one
+    scratch slot per workgroup (256 on the plan's scratch, 128 on the static
+    array), so workgroups take several blocks in turn and reuse their slot.
+    The two entry points give the same bits, and sampled outputs (all of
+    the partial block for a few channels) match the oracle."""
+    import torch
+    N, M, nchan = 65536, 16385, 300
+    L = N - M + 1
+    n = L + 777
+    say(f"partial blocks vs slots: N={N} M={M} nchan={nchan} n={n}")
+    rng = np.random.default_rng(300)
+    h = W.complex_taps(rng, M).astype(np.complex64)
+    x = W.complex_normal(rng, (nchan, n))
+    s0 = W.complex_normal(rng, (nchan, M - 1))
+    xd = to_dev(x)
+    outs = []
+    for entry in (fo.fir_ols_execute, fo.fir_ols_execute_static):
+        yd = torch.zeros_like(xd)
+        with fo.Plan(M, N, nchan) as p:
+            p.set_taps(h)
+            p.set_state(to_dev(s0))
+            entry(p.handle, xd.data_ptr(), yd.data_ptr(), n, n, None)
+            st = p.get_state().cpu().numpy()
+            p.check()
+        torch.cuda.synchronize()
+        outs.append((yd.cpu().numpy(), st))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+    y, st = outs[0]
+    idx = np.unique(np.concatenate([np.arange(300), np.arange(L - 100, n),
+                                    W.sample_indices(301, n, 300)]))
+    pick = [0, 1, 255, 256, 257, 299]              # around the slot counts
+    ref = oracle.fir_direct_multi(h, x[pick], s0[pick], idx=idx, threads=THREADS)
+    check(y[pick][:, idx], ref, h, x[pick], s0[pick], "partial blocks vs slots")
+    for c in range(nchan):
+        np.testing.assert_array_equal(st[c], oracle.state_next(x[c], s0[c], M))
