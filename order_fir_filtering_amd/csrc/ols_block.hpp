@@ -341,7 +341,9 @@ __device__ __forceinline__ void gather_block_wave(const FusedArgs &A, int64_t gb
         const __amdgpu_buffer_rsrc_t rs =
             buf_rsrc(sc, active && g0 < 0 ? (uint32_t)Mm1 * 8u : 0u);
         const int dx = (int)(g0 - xs) + tb;     // q + dx indexes x from xs
-        const int ds = (int)(g0 + Mm1) + tb;    // q + ds indexes the state
+        // q + ds indexes the state; past it (g0 >= 0, where g0 + M - 1 may
+        // not fit an int) the state descriptor is empty and ds unused
+        const int ds = (g0 < 0 ? (int)(g0 + Mm1) : 0) + tb;
         static_for<R0, R1>([&](auto Rr) {
             constexpr int off = G.TB * pass0_m<GID>(decltype(Rr)::value);
             const float2 u = buf_load_policy<NT>(rx, buf_off<8>(off + dx), 0);

@@ -382,3 +382,59 @@ def test_partial_last_blocks_outnumber_the_slots():
     check(y[pick][:, idx], ref, h, x[pick], s0[pick], "partial blocks vs slots")
     for c in range(nchan):
         np.testing.assert_array_equal(st[c], oracle.state_next(x[c], s0[c], M))
+
+
+@pytest.mark.parametrize("N,M", [(4096, 1025), (32768, 8193), (65536, 16385), (262144, 65537)])
+def test_call_beyond_two_to_the_31_samples(N, M):
+    """One channel of 2^31 + 12345 samples (17 GB in and 17 GB out, drawn
+    on the device): sample positions, block offsets and output addresses
+    pass 2^31, so every index the kernels form from them must be 64-bit.
+    Sampled outputs (the first ones, which read the state, the blocks and
+    samples around position 2^31, the partial last block, random ones) are
+    each checked against the oracle run on their own input window, and the
+    carried state against the last M - 1 samples."""
+    import torch
+    n = (1 << 31) + 12345
+    L = N - M + 1
+    say(f"beyond 2^31: N={N} M={M} n={n}")
+    rng = np.random.default_rng(N + 31)
+    h = W.complex_taps(rng, M).astype(np.complex64)
+    s0 = W.complex_normal(rng, (1, M - 1))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(N)
+    x = torch.randn(n, dtype=torch.complex64, device="cuda", generator=gen)
+    y = torch.empty_like(x)
+    with fo.Plan(M, N, 1) as p:
+        p.set_taps(h)
+        p.set_state(to_dev(s0))
+        fo.fir_ols_execute(p.handle, x.data_ptr(), y.data_ptr(), n, n, None)
+        st = p.get_state().cpu().numpy()
+        p.check()
+    torch.cuda.synchronize()
+    b31 = (1 << 31) // L
+    t = np.unique(np.concatenate([
+        np.arange(0, 48), np.arange(M - 8, M + 8),
+        np.arange(b31 * L - 24, b31 * L + 24), np.arange((1 << 31) - 24, (1 << 31) + 24),
+        np.arange(n - L // 2 - 8, n - L // 2 + 8), np.arange(n - 48, n),
+        W.sample_indices(N, n, 160)]))
+    t = t[(t >= 0) & (t < n)]
+    # the stream xt = {S0, x}: output t reads xt[t .. t + M - 1]
+    far = t[t >= M - 1]
+    win = x[torch.from_numpy(far - (M - 1)).to("cuda")[:, None]
+            + torch.arange(M, device="cuda")[None, :]].cpu().numpy()
+    got = y[torch.from_numpy(t).to("cuda")].cpu().numpy()
+    ref = np.empty(t.size, np.complex128)
+    used = []
+    xs_head = x[:M].cpu().numpy()
+    for k, tk in enumerate(t):
+        if tk >= M - 1:
+            w = win[np.searchsorted(far, tk)]
+        else:
+            w = np.concatenate([s0[0, tk:], xs_head[:tk + 1]])
+        used.append(w)
+        ref[k] = oracle.fir_direct(h, w[M - 1:], w[:M - 1])[0]
+    used = np.concatenate(used)[None, :]
+    check(got, ref, h, used, None, f"N={N} M={M} beyond 2^31")
+    np.testing.assert_array_equal(st[0], x[n - (M - 1):].cpu().numpy())
+    del x, y
+    torch.cuda.empty_cache()
