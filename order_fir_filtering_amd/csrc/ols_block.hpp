@@ -341,13 +341,14 @@ __device__ __forceinline__ void gather_block_wave(const FusedArgs &A, int64_t gb
         const __amdgpu_buffer_rsrc_t rs =
             buf_rsrc(sc, active && g0 < 0 ? (uint32_t)Mm1 * 8u : 0u);
         const int dx = (int)(g0 - xs) + tb;     // q + dx indexes x from xs
-        // q + ds indexes the state; past it (g0 >= 0, where g0 + M - 1 may
-        // not fit an int) the state descriptor is empty and ds unused
-        const int ds = (g0 < 0 ? (int)(g0 + Mm1) : 0) + tb;
+        // q + ds indexes the state (formed in 64 bits and kept unsigned:
+        // past the state, where g0 + M - 1 may not fit 32 bits, it wraps,
+        // and the state descriptor is empty there)
+        const uint32_t ds = (uint32_t)(g0 + Mm1 + tb);
         static_for<R0, R1>([&](auto Rr) {
             constexpr int off = G.TB * pass0_m<GID>(decltype(Rr)::value);
             const float2 u = buf_load_policy<NT>(rx, buf_off<8>(off + dx), 0);
-            const float2 v = buf_load_policy<NT>(rs, (uint32_t)(off + ds) * 8u, 0);
+            const float2 v = buf_load_policy<NT>(rs, ((uint32_t)off + ds) * 8u, 0);
             a[decltype(Rr)::value] = make_float2(u.x + v.x, u.y + v.y);
         });
     } else {

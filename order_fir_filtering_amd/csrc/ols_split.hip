@@ -207,10 +207,10 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
             const __amdgpu_buffer_rsrc_t rx2 = buf_rsrc(x2 + xs, (uint32_t)xn * 4u);
             const __amdgpu_buffer_rsrc_t rs = buf_rsrc(sc, g0 < 0 ? (uint32_t)Mm1 * 8u : 0u);
             const int dx = (int)(g0 - xs) + tb;
-            const int ds = (g0 < 0 ? (int)(g0 + Mm1) : 0) + tb;
+            const uint32_t ds = (uint32_t)(g0 + Mm1 + tb);   // wraps past the state (empty descriptor)
             split_gather(a, tb, [&](int j, int off) {
                 const int q = off + j * kNs;
-                const float2 v = buf_load_cached(rs, (uint32_t)(q + ds) * 8u, 0);
+                const float2 v = buf_load_cached(rs, ((uint32_t)q + ds) * 8u, 0);
                 return make_float2(buf_load_f32_cached(rx1, buf_off<4>(q + dx), 0) + v.x,
                                    buf_load_f32_cached(rx2, buf_off<4>(q + dx), 0) + v.y);
             }, wt, wm, ra1);
@@ -224,11 +224,12 @@ __global__ __launch_bounds__(kBig.TB) void ols_split_kernel(SplitArgs A) {
             const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xc + xs, (uint32_t)xn * 8u);
             const __amdgpu_buffer_rsrc_t rs = buf_rsrc(sc, g0 < 0 ? (uint32_t)Mm1 * 8u : 0u);
             const int dx = (int)(g0 - xs) + tb;     // q + dx indexes x from xs
-            const int ds = (g0 < 0 ? (int)(g0 + Mm1) : 0) + tb;  // q + ds indexes the state
+            // q + ds indexes the state (wraps past it: empty descriptor there)
+            const uint32_t ds = (uint32_t)(g0 + Mm1 + tb);
             split_gather(a, tb, [&](int j, int off) {
                 const int q = off + j * kNs;
                 const float2 u = buf_load_cached(rx, buf_off<8>(q + dx), 0);
-                const float2 v = buf_load_cached(rs, (uint32_t)(q + ds) * 8u, 0);
+                const float2 v = buf_load_cached(rs, ((uint32_t)q + ds) * 8u, 0);
                 return make_float2(u.x + v.x, u.y + v.y);
             }, wt, wm, ra1);
         }
