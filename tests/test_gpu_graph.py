@@ -68,3 +68,59 @@ def test_graph_replays_equal_eager_calls(N, M, nchan):
             yg.copy_(x * 2)
             torch.cuda.synchronize()
         del g
+
+
+@pytest.mark.parametrize("entry", ["static", "real"])
+@pytest.mark.parametrize("N,M", [(4096, 1025), (65536, 16385), (131072, 40000)])
+def test_graph_replays_of_static_and_real_entry_points(entry, N, M):
+    """The same replay check for fir_ols_execute_static (scratch in the
+    library's fixed array, the entry meant for capture) and for
+    fir_ols_execute_real (two float rows per channel, real taps)."""
+    import torch
+    say(f"graph {entry}: N={N} M={M}")
+    rng = np.random.default_rng(N + M + (7 if entry == "real" else 0))
+    nchan = 2
+    L = N - M + 1
+    calls = [2 * L + 5, L - 3]
+    n = sum(calls)
+    if entry == "real":
+        h = (rng.standard_normal(M) / np.sqrt(M)).astype(np.float32)
+        x = to_dev(rng.standard_normal((2 * nchan, n)).astype(np.float32))
+        fn, item = fo.fir_ols_execute_real, 4
+    else:
+        h = W.complex_taps(rng, M).astype(np.complex64)
+        x = to_dev(W.complex_normal(rng, (nchan, n)))
+        fn, item = fo.fir_ols_execute_static, 8
+    stream = torch.cuda.Stream()
+    reps = 3
+
+    def run(p, y):
+        pos = 0
+        for c in calls:
+            fn(p.handle, x.data_ptr() + item * pos, y.data_ptr() + item * pos, c, n,
+               stream.cuda_stream)
+            pos += c
+
+    want = []
+    with fo.Plan(M, N, nchan) as pe:
+        pe.set_taps(h)
+        for _ in range(reps):
+            y = torch.zeros_like(x)
+            run(pe, y)
+            stream.synchronize()
+            want.append(y.cpu().numpy())
+    assert not np.array_equal(want[0], want[1])
+
+    with fo.Plan(M, N, nchan) as pg:
+        pg.set_taps(h)
+        yg = torch.zeros_like(x)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            run(pg, yg)
+        for r in range(reps):
+            g.replay()
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(yg.cpu().numpy(), want[r])
+            yg.copy_(x * 2)
+            torch.cuda.synchronize()
+        del g
