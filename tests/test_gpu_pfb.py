@@ -233,3 +233,38 @@ def test_pfb_graph_replays_equal_eager_calls():
             yg.copy_(yg * 2)                          # unrelated eager work
             torch.cuda.synchronize()
         del g
+
+
+@pytest.mark.parametrize("k", range(12))
+def test_pfb_random_cases(k):
+    """Seeded random draws: K = 64 .. 1024, D = K / 1 .. K / 8, Nh from 1 to
+    8 K, one to four calls of random multiples of D, and either a random
+    state with a stream time up to 2^40 or the zero start.  Outputs at the
+    start, around each call boundary, at the end and at random are checked
+    against the oracle, then the state and the stream time."""
+    rng = np.random.default_rng(40_000 + k)
+    K = 1 << int(rng.integers(6, 11))
+    D = K >> int(rng.integers(0, 4))
+    Nh = int(rng.choice([1, int(rng.integers(2, K + 1)), int(rng.integers(K, 8 * K + 1)), 8 * K]))
+    calls = [int(rng.choice([1, 2, int(rng.integers(1, 40)), int(rng.integers(40, 400))])) * D
+             for _ in range(int(rng.integers(1, 5)))]
+    n = sum(calls)
+    use_state = bool(rng.integers(0, 2))
+    t0 = int(rng.integers(0, 1 << 40)) if use_state else None
+    say(f"pfb random {k}: K={K} D={D} Nh={Nh} calls={[c // D for c in calls]}xD t0={t0}")
+    h = (rng.standard_normal(Nh) / np.sqrt(Nh)).astype(np.float32)
+    x = W.complex_normal(rng, n)
+    st = W.complex_normal(rng, Nh - 1) if use_state else None
+    y, st_next, t = run(K, D, h, x, calls, state=st if use_state and Nh > 1 else None,
+                        t_next=t0)
+    nout = n // D
+    edges = np.cumsum([c // D for c in calls])[:-1]
+    idx = np.unique(np.concatenate(
+        [np.arange(min(nout, 8)), np.arange(max(0, nout - 8), nout),
+         np.concatenate([np.arange(max(0, b - 2), min(nout, b + 2)) for b in edges])
+         if len(edges) else np.zeros(0, np.int64),
+         rng.integers(0, nout, size=min(nout, 24))]))
+    ref = oracle.pfb_channelize(h, x, K, D, state=st, t0=t0 or 0, idx=idx)
+    check(y[idx], ref, h, x, st, f"K={K} D={D} Nh={Nh}")
+    np.testing.assert_array_equal(st_next, oracle.pfb_state_next(x, st, Nh))
+    assert t == (t0 or 0) + n
