@@ -438,3 +438,61 @@ def test_call_beyond_two_to_the_31_samples(N, M):
     np.testing.assert_array_equal(st[0], x[n - (M - 1):].cpu().numpy())
     del x, y
     torch.cuda.empty_cache()
+
+
+def test_plans_on_concurrent_streams_equal_their_sequential_runs():
+    """Three plans (two at N = 65536, one at N = 32768) each on its own
+    stream, their calls enqueued interleaved with no synchronization in
+    between, so the kernels can run at the same time and share the CUs:
+    each plan's outputs and state are bitwise those of the same calls run
+    alone (each plan has its own scratch, queues and flags, and a paired
+    consumer only waits on a producer that is already running)."""
+    import torch
+    specs = [(65536, 16385, 1, 200), (65536, 4097, 2, 150), (32768, 8193, 1, 300)]
+    rng = np.random.default_rng(555)
+    setups = []
+    for N, M, nchan, nblk in specs:
+        L = N - M + 1
+        n = nblk * L + L // 2
+        h = W.complex_taps(rng, M).astype(np.complex64)
+        x = to_dev(W.complex_normal(rng, (nchan, n)))
+        s0 = to_dev(W.complex_normal(rng, (nchan, M - 1)))
+        calls = [n // 3, n // 3, n - 2 * (n // 3)]
+        setups.append((N, M, nchan, n, h, x, s0, calls))
+
+    def run_all(concurrent):
+        plans, outs, streams = [], [], []
+        for N, M, nchan, n, h, x, s0, calls in setups:
+            p = fo.Plan(M, N, nchan)
+            p.set_taps(h)
+            p.set_state(s0)
+            plans.append(p)
+            outs.append(torch.zeros_like(x))
+            streams.append(torch.cuda.Stream())
+        torch.cuda.synchronize()
+        order = ([(k, j) for j in range(3) for k in range(len(setups))] if concurrent
+                 else [(k, j) for k in range(len(setups)) for j in range(3)])
+        pos = [0] * len(setups)
+        for k, j in order:
+            N, M, nchan, n, h, x, s0, calls = setups[k]
+            c = calls[j]
+            fo.fir_ols_execute(plans[k].handle, x.data_ptr() + 8 * pos[k],
+                               outs[k].data_ptr() + 8 * pos[k], c, n, streams[k].cuda_stream)
+            pos[k] += c
+            if not concurrent:
+                streams[k].synchronize()
+        res = []
+        for k, p in enumerate(plans):
+            st = p.get_state(streams[k])
+            streams[k].synchronize()
+            p.check()
+            res.append((outs[k].cpu().numpy(), st.cpu().numpy()))
+            p.close()
+        return res
+
+    alone = run_all(False)
+    together = run_all(True)
+    for (ya, sa), (yt, st), spec in zip(alone, together, specs):
+        say(f"  concurrent plan {spec}: outputs and state compared")
+        np.testing.assert_array_equal(yt, ya)
+        np.testing.assert_array_equal(st, sa)
